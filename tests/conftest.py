@@ -1,0 +1,15 @@
+"""Shared test configuration: markers and the repository root on sys.path."""
+
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; run through the GPU runner")
+    config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
