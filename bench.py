@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the signaling-GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: the signaling GEMM
+(stream A) with the consumer and the post-communication reorder (stream B)
+running beside it, linked only by the device signals.  Inputs are seeded and
+synthetic and already resident in HBM when the timed region starts.
+
+Default workload: the profiled GEMM shape of the pages' wave-pattern figure,
+M = 2048, N = K = 8192, bf16, 256 x 128 tiles, 512 tiles over 256 CUs (two
+waves), partitions (2) and (1, 1).  ``value`` is useful GEMM TFLOP/s of the
+whole step (2 M N K per step / step time) for the best partition.
+
+Prints one JSON line.  Extra fields: the signaling and plain GEMMs measured
+alone, their ratio, the consumer's and the post-reorder's HBM GB/s (MALL
+flushed before each timed launch), per-partition step rates, and the oracle
+timed on the host cores as a CPU baseline (rank 0, N = 1).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="profiled")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle's CPU sample (0 = auto)")
+    return ap.parse_args()
+
+
+def _event_pairs(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def _flush_mall(torch, scratch):
+    scratch.fill_(1)        # writes 512 MiB: evicts the 256 MB memory-side cache
+
+
+def _time_kernel(torch, launch, stream, n, scratch=None):
+    """Average duration (ms) of ``launch(stream)`` over n launches, HIP events on that stream."""
+    ev = _event_pairs(torch, n)
+    for i in range(n):
+        if scratch is not None:
+            with torch.cuda.stream(stream):
+                _flush_mall(torch, scratch)
+        ev[i][0].record(stream)
+        launch(stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, rows):
+    """The oracle pipeline (fp64 GEMM, pre-reorder, consumer, post-reorder) on the first ``rows`` rows."""
+    import oracle
+    from oracle.tiles import make_plan
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    rows = min(rows, w.M)
+    T_s = -(-(-(-rows // w.BM) * -(-w.N // w.BN)) // w.W)
+    plan = make_plan([rows], w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=(T_s,), mode="tile")
+    t0 = time.perf_counter()
+    oracle.run_pipeline(A[:rows], B, peer[: rows * w.N], plan, w.dtype)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"first {rows} of {w.M} rows (M={rows}, N={w.N}, K={w.K}), one group; {dt:.2f} s")
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {a.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_tile_signaling_amd as fo
+    from gemm_tile_signaling_amd.pipeline import Pipeline
+    from workloads import WORKLOADS, make_inputs, to_bits, draw
+
+    w = WORKLOADS[a.workload]
+    if w.experts:
+        raise SystemExit("the benchmark line is quoted on a single-problem workload")
+    A, B, peer, m_per, row_dest = make_inputs(w)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A.view(np.int16).reshape(-1).copy()).to(dev)
+    dB = torch.from_numpy(np.concatenate([b.reshape(-1) for b in B]).view(np.int16).copy()).to(dev)
+    dpeer = torch.from_numpy(peer.view(np.int16).copy()).to(dev)
+    flops = 2.0 * w.M * w.N * w.K
+    comps = list(w.compositions) or [None]
+    scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.int32, device=dev)
+
+    results = []
+    for comp in comps:
+        plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W,
+                       composition=comp, mode=w.mode, ranks=w.ranks, row_dest=row_dest)
+        pipe = Pipeline(plan, dA, dB, dpeer)
+        for _ in range(a.warmup):
+            pipe.step()
+        pipe.join()
+        torch.cuda.synchronize()
+        evs = {k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")}
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            pipe.step(events={k: v[i] for k, v in evs.items()})
+        pipe.join()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if int(pipe.status.item()) != 0:
+            raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
+        avg = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in evs.items()}
+        results.append(dict(plan=plan, pipe=pipe, comp=comp or tuple([1] * plan.T), step_ms=el * 1e3 / a.steps,
+                            gemm_ms=avg["gemm"], consume_ms=avg["consume"], post_ms=avg["post"]))
+    best = min(results, key=lambda r: r["step_ms"])
+    plan, pipe = best["plan"], best["pipe"]
+
+    # kernels alone (same plan), each timed with HIP events on its own stream
+    s = torch.cuda.Stream(device=dev)
+    n_alone = max(10, min(a.steps, 50))
+    C = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
+    plain_ms = _time_kernel(torch, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, n_alone)
+    sig = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
+    ep = [0]
+
+    def _sig(st):
+        ep[0] += 1
+        plan.gemm_signal(dA, dB, pipe.buf, sig, ep[0], stream=st)
+    signal_ms = _time_kernel(torch, _sig, s, n_alone)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ready = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
+    ready[plan.P:] = 1
+    recv = torch.empty_like(pipe.buf)
+    consume_ms = _time_kernel(torch, lambda st: plan.consume_group(pipe.buf, dpeer, recv, ready, 1, status, stream=st),
+                              s, n_alone, scratch)
+    post_ms = _time_kernel(torch, lambda st: plan.reorder_post(recv, C, stream=st), s, n_alone, scratch)
+    mn = w.M * w.N
+    consume_gbps = 6.0 * mn / (consume_ms * 1e-3) / 1e9
+    post_gbps = 4.0 * mn / (post_ms * 1e-3) / 1e9
+
+    achieved = flops / (best["gemm_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "signaling-GEMM TFLOP/s (% of plain GEMM & MFMA peak); reorder HBM GB/s",
+        "value": round(flops / (best["step_ms"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(best["step_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: GEMM M={w.M} N={w.N} K={w.K} {w.dtype}, {w.BM}x{w.BN} tiles, "
+                               f"swizzle {w.S}, wave {w.W} tiles, groups {tuple(best['comp'])}, "
+                               f"consumer copy+add, post-reorder",
+                   "M": w.M, "N": w.N, "K": w.K, "tile": [w.BM, w.BN], "swizzle": w.S, "wave": w.W,
+                   "tiles": plan.NT, "waves": plan.T, "groups": list(best["comp"]), "parallelism": "1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "signaling GEMM (stream A, consumer resident)"},
+        "signal_gemm_alone_tflops": round(flops / (signal_ms * 1e-3) / 1e12, 2),
+        "plain_gemm_alone_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
+        "signal_over_plain_alone": round(plain_ms / signal_ms, 4),
+        "signal_with_consumer_over_plain": round(plain_ms / best["gemm_ms"], 4),
+        "consumer_alone_gbps": round(consume_gbps, 1),
+        "post_reorder_alone_gbps": round(post_gbps, 1),
+        "consumer_frac_hbm": round(consume_gbps / PEAK_HBM_GBPS, 4),
+        "post_reorder_frac_hbm": round(post_gbps / PEAK_HBM_GBPS, 4),
+        "partitions": [{"groups": list(r["comp"]), "step_ms": round(r["step_ms"], 4),
+                        "gemm_ms": round(r["gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
+                        "post_ms": round(r["post_ms"], 4)} for r in results],
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        rows = a.cpu_rows or 512
+        line["cpu_baseline"] = cpu_baseline(w, A, B, peer, m_per, row_dest, comps[0], rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

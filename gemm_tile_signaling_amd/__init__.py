@@ -1,0 +1,253 @@
+"""Python binding of libfo, the signaling GEMM with tile reordering for MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libfo.so`` (built by ``gemm_tile_signaling_amd/build.py``).  There is no
+fallback: if the library is missing, importing the binding's entry points
+raises.  PyTorch supplies device memory and streams; any object with
+``data_ptr()`` (a torch tensor) or a plain integer address is accepted as a
+buffer.
+
+The names follow the C ABI in ``include/fo.h``: ``Plan`` wraps
+``fo_plan_groups``; its methods ``gemm_signal``, ``gemm_plain``,
+``consume_group``, ``reorder_post`` and ``reorder_pre`` wrap the enqueue
+calls of the same names.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = ["Plan", "FoError", "lib", "LIB_PATH", "status_string",
+           "FO_OK", "FO_ERR_INVALID", "FO_ERR_UNSUPPORTED", "FO_ERR_HIP", "FO_ERR_NOMEM", "FO_ERR_TIMEOUT"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
+
+FO_OK, FO_ERR_INVALID, FO_ERR_UNSUPPORTED, FO_ERR_HIP, FO_ERR_NOMEM, FO_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
+_DTYPES = {"bf16": 0, "fp16": 1}
+_MODES = {"tile": 0, "subtile": 1, "subtoken": 2}
+FO_PLAN_HOST_ONLY = 1
+
+
+class FoError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+        self.code = code
+
+
+class _Desc(C.Structure):
+    _fields_ = [
+        ("num_problems", C.c_int32), ("m_per_problem", C.POINTER(C.c_int64)),
+        ("N", C.c_int64), ("K", C.c_int64),
+        ("dtype", C.c_int32), ("BM", C.c_int32), ("BN", C.c_int32), ("swizzle", C.c_int32),
+        ("wave_size", C.c_int32), ("num_groups", C.c_int32), ("waves_per_group", C.POINTER(C.c_int32)),
+        ("mode", C.c_int32), ("ranks", C.c_int32), ("row_dest", C.POINTER(C.c_int32)),
+        ("dispatch_order", C.POINTER(C.c_int32)), ("flags", C.c_uint32),
+    ]
+
+
+class _Info(C.Structure):
+    _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64)] + [
+        (n, C.c_int32) for n in ("BM", "BN", "swizzle", "wave_size", "NT", "T", "P", "num_units",
+                                 "mode", "ranks", "dtype", "num_problems", "device")]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libfo.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run gemm_tile_signaling_amd/build.py "
+                              "(or __graft_entry__.build()) first; there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, u32, i64, u64 = C.c_void_p, C.c_int32, C.c_uint32, C.c_int64, C.c_uint64
+        sig = {
+            "fo_plan_groups": [C.POINTER(_Desc), C.POINTER(vp)],
+            "fo_plan_destroy": [vp],
+            "fo_plan_info_get": [vp, C.POINTER(_Info)],
+            "fo_plan_tables": [vp, vp, vp, vp, vp, vp],
+            "fo_plan_units": [vp, vp, vp],
+            "fo_plan_offsets": [vp, vp],
+            "fo_gemm_signal": [vp, vp, vp, vp, vp, u32, vp, vp],
+            "fo_gemm_plain": [vp, vp, vp, vp, vp],
+            "fo_consume_group": [vp, vp, vp, vp, vp, u32, i32, i32, vp, u64, i32, vp],
+            "fo_reorder_post": [vp, vp, vp, vp],
+            "fo_reorder_pre": [vp, vp, vp, vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = C.c_int
+        L.fo_status_string.argtypes = [C.c_int]
+        L.fo_status_string.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().fo_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != FO_OK:
+        raise FoError(code, what)
+
+
+def _arr(a, ctype):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a), dtype={C.c_int32: np.int32, C.c_int64: np.int64}[ctype])
+    return arr, arr.ctypes.data_as(C.POINTER(ctype))
+
+
+def _ptr(x, *, numel: Optional[int] = None, itemsize: Optional[int] = None, name: str = "buffer") -> int:
+    """Device address of a buffer; checks size, element width and contiguity of torch tensors."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if hasattr(x, "is_contiguous") and not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if hasattr(x, "is_cuda") and not x.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if itemsize is not None and x.element_size() != itemsize:
+            raise ValueError(f"{name}: element size {x.element_size()} != {itemsize}")
+        if numel is not None and x.numel() < numel:
+            raise ValueError(f"{name}: {x.numel()} elements < {numel} required")
+        return int(x.data_ptr())
+    raise TypeError(f"{name}: expected a tensor or an address")
+
+
+def _stream(s) -> int:
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+class Plan:
+    """A wave-group plan (``fo_plan_groups``): tables built once, uploaded once.
+
+    ``m_per_problem``: rows of each problem (an int for a plain GEMM).
+    ``composition``: waves per group (a partition of T); None = one wave per group.
+    ``host_only``: build the tables without a GPU (the enqueue calls then refuse it).
+    """
+
+    def __init__(self, m_per_problem, N: int, K: int, dtype: str = "bf16", *, BM: int = 0, BN: int = 0,
+                 swizzle: int = 0, wave_size: int = 0, composition: Optional[Sequence[int]] = None,
+                 mode: str = "tile", ranks: int = 1, row_dest=None, dispatch_order=None, host_only: bool = False):
+        L = lib()
+        if isinstance(m_per_problem, (int, np.integer)):
+            m_per_problem = [int(m_per_problem)]
+        self._m, mp = _arr(list(m_per_problem), C.c_int64)
+        self._comp, cp = _arr(list(composition) if composition is not None else None, C.c_int32)
+        self._rd, rp = _arr(row_dest, C.c_int32)
+        self._do, dp = _arr(dispatch_order, C.c_int32)
+        d = _Desc(num_problems=len(self._m), m_per_problem=mp, N=int(N), K=int(K), dtype=_DTYPES[dtype],
+                  BM=int(BM), BN=int(BN), swizzle=int(swizzle), wave_size=int(wave_size),
+                  num_groups=len(self._comp) if self._comp is not None else 0, waves_per_group=cp,
+                  mode=_MODES[mode], ranks=int(ranks), row_dest=rp, dispatch_order=dp,
+                  flags=FO_PLAN_HOST_ONLY if host_only else 0)
+        h = C.c_void_p()
+        _check(L.fo_plan_groups(C.byref(d), C.byref(h)), "fo_plan_groups")
+        self._h = h
+        info = _Info()
+        _check(L.fo_plan_info_get(h, C.byref(info)), "fo_plan_info_get")
+        self.info = {n: getattr(info, n) for n, _ in _Info._fields_}
+        self.dtype = dtype
+        self.mode = mode
+        for k in ("M", "N", "K", "BM", "BN", "NT", "T", "P", "num_units"):
+            setattr(self, k, self.info[k])
+        self.W = self.info["wave_size"]
+        self.S = self.info["swizzle"]
+        self.num_problems = self.info["num_problems"]
+
+    # ------------------------------------------------------------------ host-side tables
+    def tables(self) -> dict:
+        NT, P = self.NT, self.P
+        t_of_s = np.zeros(NT, np.int32)
+        s_of_t = np.zeros(NT, np.int32)
+        g_of_s = np.zeros(NT, np.int32)
+        g_tiles = np.zeros(P, np.int32)
+        span = np.zeros(P + 1, np.int64)
+        _check(lib().fo_plan_tables(self._h, t_of_s.ctypes.data, s_of_t.ctypes.data, g_of_s.ctypes.data,
+                                    g_tiles.ctypes.data, span.ctypes.data), "fo_plan_tables")
+        return dict(tile_of_slot=t_of_s, slot_of_tile=s_of_t, group_of_slot=g_of_s, group_tiles=g_tiles,
+                    span_off=span)
+
+    def units(self):
+        uo = np.zeros(self.num_units + 1, np.int64)
+        gu = np.zeros(self.P + 1, np.int32)
+        _check(lib().fo_plan_units(self._h, uo.ctypes.data, gu.ctypes.data), "fo_plan_units")
+        return uo, gu
+
+    def offsets(self) -> np.ndarray:
+        off = np.full((self.M, self.N), -1, np.int64)
+        _check(lib().fo_plan_offsets(self._h, off.ctypes.data if off.size else None), "fo_plan_offsets")
+        return off
+
+    # ------------------------------------------------------------------ enqueue calls
+    @property
+    def mn(self) -> int:
+        return self.M * self.N
+
+    def gemm_signal(self, A, B, reorder_buf, sig, epoch: int, trace=None, stream=None):
+        _check(lib().fo_gemm_signal(
+            self._h, _ptr(A, numel=self.M * self.K, itemsize=2, name="A"),
+            _ptr(B, numel=self.num_problems * self.N * self.K, itemsize=2, name="B"),
+            _ptr(reorder_buf, numel=self.mn, itemsize=2, name="reorder_buf"),
+            _ptr(sig, numel=2 * self.P, itemsize=4, name="sig"), int(epoch),
+            _ptr(trace, numel=2 * self.NT + self.P, itemsize=8, name="trace"), _stream(stream)), "fo_gemm_signal")
+
+    def gemm_plain(self, A, B, Cout, stream=None):
+        _check(lib().fo_gemm_plain(
+            self._h, _ptr(A, numel=self.M * self.K, itemsize=2, name="A"),
+            _ptr(B, numel=self.num_problems * self.N * self.K, itemsize=2, name="B"),
+            _ptr(Cout, numel=self.mn, itemsize=2, name="C"), _stream(stream)), "fo_gemm_plain")
+
+    def consume_group(self, send, peer, recv, sig, epoch: int, status, g_begin: int = 0, g_end: Optional[int] = None,
+                      timeout_us: int = 0, num_workgroups: int = 0, stream=None):
+        g_end = self.P if g_end is None else g_end
+        _check(lib().fo_consume_group(
+            self._h, _ptr(send, numel=self.mn, itemsize=2, name="send"),
+            _ptr(peer, numel=self.mn, itemsize=2, name="peer"), _ptr(recv, numel=self.mn, itemsize=2, name="recv"),
+            _ptr(sig, numel=2 * self.P, itemsize=4, name="sig"), int(epoch), int(g_begin), int(g_end),
+            _ptr(status, numel=1, itemsize=4, name="status"), int(timeout_us), int(num_workgroups),
+            _stream(stream)), "fo_consume_group")
+
+    def reorder_post(self, reordered, out, stream=None):
+        _check(lib().fo_reorder_post(self._h, _ptr(reordered, numel=self.mn, itemsize=2, name="reordered"),
+                                     _ptr(out, numel=self.mn, itemsize=2, name="out"), _stream(stream)),
+               "fo_reorder_post")
+
+    def reorder_pre(self, rowmajor, reordered, stream=None):
+        _check(lib().fo_reorder_pre(self._h, _ptr(rowmajor, numel=self.mn, itemsize=2, name="in"),
+                                    _ptr(reordered, numel=self.mn, itemsize=2, name="reordered"), _stream(stream)),
+               "fo_reorder_pre")
+
+    # ------------------------------------------------------------------ lifetime
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            lib().fo_plan_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()

@@ -1,0 +1,69 @@
+// Enqueue calls of the C ABI: argument checks on the host, then the launchers.
+// Nothing here allocates, copies from the host or synchronises.
+#include <cstdint>
+
+#include "fo_internal.h"
+
+namespace {
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool device_ready(const fo_plan *p) { return p && !p->host_only && p->dev_block; }
+
+// a buffer of M*N elements must be present and 16-byte aligned unless it is empty
+bool buf_ok(const fo_plan *p, const void *ptr) { return (p->M * p->N == 0) || (ptr && aligned16(ptr)); }
+
+}  // namespace
+
+extern "C" {
+
+int fo_gemm_signal(const fo_plan *p, const void *A, const void *B, void *reorder_buf, uint32_t *sig, uint32_t epoch,
+                   uint64_t *trace, hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (p->NT == 0) return FO_OK;
+  if (!A || !B || !aligned16(A) || !aligned16(B) || !buf_ok(p, reorder_buf)) return FO_ERR_INVALID;
+  if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return FO_ERR_INVALID;
+  if (trace && (reinterpret_cast<uintptr_t>(trace) & 7u)) return FO_ERR_INVALID;
+  int32_t max_g = 0;
+  for (int32_t v : p->group_tiles) max_g = v > max_g ? v : max_g;
+  if ((uint64_t)epoch * (uint64_t)max_g > 0xFFFFFFFFull) return FO_ERR_INVALID;
+  return fo::launch_gemm(p, A, B, reorder_buf, false, sig, epoch, trace, stream);
+}
+
+int fo_gemm_plain(const fo_plan *p, const void *A, const void *B, void *C, hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (p->NT == 0) return FO_OK;
+  if (!A || !B || !aligned16(A) || !aligned16(B) || !buf_ok(p, C)) return FO_ERR_INVALID;
+  return fo::launch_gemm(p, A, B, C, true, nullptr, 0, nullptr, stream);
+}
+
+int fo_consume_group(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
+                     uint32_t epoch, int32_t g_begin, int32_t g_end, int32_t *dev_status, uint64_t timeout_us,
+                     int32_t num_workgroups, hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (g_begin < 0 || g_end > p->P || g_begin > g_end) return FO_ERR_INVALID;
+  if (g_begin == g_end) return FO_OK;
+  if (!buf_ok(p, send) || !buf_ok(p, peer) || !buf_ok(p, recv)) return FO_ERR_INVALID;
+  if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return FO_ERR_INVALID;
+  if (!dev_status || (reinterpret_cast<uintptr_t>(dev_status) & 3u)) return FO_ERR_INVALID;
+  if (num_workgroups < 0 || num_workgroups > 65536) return FO_ERR_INVALID;
+  const int32_t grid = num_workgroups ? num_workgroups : (p->num_cus > 0 ? p->num_cus : 256);
+  const uint64_t us = timeout_us ? timeout_us : 2000000ull;
+  if (us > (1ull << 40)) return FO_ERR_INVALID;
+  return fo::launch_consume(p, send, peer, recv, sig, epoch, g_begin, g_end, dev_status, us * p->ticks_per_us, grid,
+                            stream);
+}
+
+int fo_reorder_post(const fo_plan *p, const void *reordered, void *out, hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (!buf_ok(p, reordered) || !buf_ok(p, out)) return FO_ERR_INVALID;
+  return fo::launch_reorder(p, reordered, out, true, stream);
+}
+
+int fo_reorder_pre(const fo_plan *p, const void *in, void *reordered, hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (!buf_ok(p, in) || !buf_ok(p, reordered)) return FO_ERR_INVALID;
+  return fo::launch_reorder(p, in, reordered, false, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Consumer: waits on the device for each wave group's signal, then reduces the
+// group's contiguous span with a second buffer -- the one-GPU stand-in for the
+// group's collective call.
+//
+// Method: deep-dive page "FlashOverlap: 信号驱动计算通信重叠论文详解",
+//   五、CUTLASS 扩展实现 › 专用监控内核 -- progress is tracked through atomic
+//   counters and communication runs on its own stream, notified by the
+//   signals; 核心设计 › 通信侧 and 二 › (1) AllReduce (code box) -- the
+//   contiguous span is handed to one collective call.
+//
+// Design: a persistent grid.  Every workgroup walks the groups in firing
+// order; for each group one lane polls flag[g] (agent-scope loads, s_sleep
+// back-off, bounded by the device wall clock), the workgroup meets at a
+// barrier and acquires device scope, and then all workgroups stream the
+// group's units with 16-byte loads: recv = round(float(send) + float(peer)).
+// The kernel holds no LDS beyond one word and few registers, so it can stay
+// resident next to the GEMM's workgroups.
+#include "../fo_internal.h"
+
+namespace fo {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+struct ConsumeParams {
+  const uint16_t *send;
+  const uint16_t *peer;
+  uint16_t *recv;
+  const uint32_t *flag;
+  const int64_t *unit_off;
+  const int32_t *group_unit;
+  int32_t *status;
+  uint64_t timeout_ticks;
+  uint32_t epoch;
+  int32_t g_begin, g_end;
+};
+
+template <typename T>
+__device__ __forceinline__ u32x4 add8(u32x4 a, u32x4 b);
+template <>
+__device__ __forceinline__ u32x4 add8<__bf16>(u32x4 a, u32x4 b) {
+  const f32x8 x = __builtin_convertvector(__builtin_bit_cast(bf16x8, a), f32x8);
+  const f32x8 y = __builtin_convertvector(__builtin_bit_cast(bf16x8, b), f32x8);
+  return __builtin_bit_cast(u32x4, __builtin_convertvector(x + y, bf16x8));
+}
+template <>
+__device__ __forceinline__ u32x4 add8<_Float16>(u32x4 a, u32x4 b) {
+  const f32x8 x = __builtin_convertvector(__builtin_bit_cast(f16x8, a), f32x8);
+  const f32x8 y = __builtin_convertvector(__builtin_bit_cast(f16x8, b), f32x8);
+  return __builtin_bit_cast(u32x4, __builtin_convertvector(x + y, f16x8));
+}
+
+// flag values only grow, one step per launch; compare as a signed distance
+__device__ __forceinline__ bool reached(uint32_t v, uint32_t epoch) { return (int32_t)(v - epoch) >= 0; }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
+  __shared__ int s_go;
+  const int tid = threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int g = p.g_begin; g < p.g_end; ++g) {
+    if (tid == 0) {
+      int go = 1;
+      if (!reached(__hip_atomic_load(&p.flag[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), p.epoch)) {
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+          __builtin_amdgcn_s_sleep(2);
+          if (reached(__hip_atomic_load(&p.flag[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), p.epoch)) break;
+          if (__hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            go = 0;  // another workgroup gave up
+            break;
+          }
+          if (wall_clock64() - t0 > p.timeout_ticks) {
+            int expected = 0;
+            __hip_atomic_compare_exchange_strong(p.status, &expected, (int)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            go = 0;
+            break;
+          }
+        }
+      }
+      s_go = go;
+    }
+    __syncthreads();
+    const int go = s_go;
+    __syncthreads();  // s_go is rewritten for the next group
+    if (!go) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the producer's tile stores become visible
+
+    for (int u = p.group_unit[g]; u < p.group_unit[g + 1]; ++u) {
+      const int64_t lo = p.unit_off[u] >> 3, hi = p.unit_off[u + 1] >> 3;  // 16-byte chunks
+      for (int64_t c0 = lo + (int64_t)blockIdx.x * kThreads + tid; c0 < hi; c0 += kUnroll * stride) {
+        u32x4 a[kUnroll], b[kUnroll];
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+          const int64_t c = c0 + i * stride;
+          if (c < hi) {
+            a[i] = *reinterpret_cast<const u32x4 *>(p.send + c * 8);
+            b[i] = *reinterpret_cast<const u32x4 *>(p.peer + c * 8);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+          const int64_t c = c0 + i * stride;
+          if (c < hi) *reinterpret_cast<u32x4 *>(p.recv + c * 8) = add8<T>(a[i], b[i]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_consume(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
+                   uint32_t epoch, int32_t g_begin, int32_t g_end, int32_t *status, uint64_t timeout_ticks,
+                   int32_t grid, hipStream_t s) {
+  if (g_begin >= g_end) return FO_OK;
+  ConsumeParams cp{};
+  cp.send = static_cast<const uint16_t *>(send);
+  cp.peer = static_cast<const uint16_t *>(peer);
+  cp.recv = static_cast<uint16_t *>(recv);
+  cp.flag = sig + p->P;
+  cp.unit_off = p->d_unit_off;
+  cp.group_unit = p->d_group_unit;
+  cp.status = status;
+  cp.timeout_ticks = timeout_ticks;
+  cp.epoch = epoch;
+  cp.g_begin = g_begin;
+  cp.g_end = g_end;
+  if (p->dtype == FO_BF16)
+    hipLaunchKernelGGL(consume_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, s, cp);
+  else
+    hipLaunchKernelGGL(consume_kernel<_Float16>, dim3(grid), dim3(kThreads), 0, s, cp);
+  return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
+}
+
+}  // namespace fo

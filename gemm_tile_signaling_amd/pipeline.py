@@ -1,0 +1,84 @@
+"""One pass of the hot path on two HIP streams, built from the C-ABI calls.
+
+Stream A runs the signaling GEMM; stream B runs the consumer and then the
+post-communication reorder.  The two streams are linked on the device only
+through the signal words (counting table + flags); the host orders only
+consecutive passes (the next GEMM reuses the reordered buffer, so stream A
+waits for the previous pass's reorder to finish).
+
+Launch order: the GEMM is enqueued before the consumer.  The GEMM never
+waits for anything, so even if both streams ended up on one hardware queue
+the pass would complete (serialised, without overlap).
+
+Buffers (torch tensors, 16-bit elements stored as int16):
+  A [M*K], B [problems*N*K], reorder_buf / peer / recv / out [M*N],
+  sig int32 [2P] (zeroed once; epochs count up), status int32 [1].
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+from . import Plan
+
+
+class Pipeline:
+    def __init__(self, plan: Plan, A, B, peer, *, consumer_workgroups: int = 0, timeout_us: int = 0,
+                 in_place: bool = False):
+        import torch
+        self.torch = torch
+        self.plan = plan
+        n = plan.M * plan.N
+        dev = A.device
+        self.A, self.B, self.peer = A, B, peer
+        self.buf = torch.empty(n, dtype=torch.int16, device=dev)
+        self.recv = self.buf if in_place else torch.empty(n, dtype=torch.int16, device=dev)
+        self.out = torch.empty(n, dtype=torch.int16, device=dev)
+        self.sig = torch.zeros(max(1, 2 * plan.P), dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.sa = torch.cuda.Stream(device=dev)
+        self.sb = torch.cuda.Stream(device=dev)
+        self.done_b = torch.cuda.Event()
+        self.epoch = 0
+        self.consumer_workgroups = consumer_workgroups
+        self.timeout_us = timeout_us
+        # inputs were produced on the current stream
+        ready = torch.cuda.Event()
+        ready.record(torch.cuda.current_stream(dev))
+        self.sa.wait_event(ready)
+        self.sb.wait_event(ready)
+        self.done_b.record(self.sb)
+
+    def step(self, trace=None, events: Optional[dict] = None):
+        """Enqueue one pass; returns the epoch it used.  ``events`` may hold
+        torch.cuda.Event pairs recorded around each kernel on its own stream:
+        keys 'gemm', 'consume', 'post' -> (start, end)."""
+        p = self.plan
+        self.epoch += 1
+        e = self.epoch
+        self.sa.wait_event(self.done_b)
+        if events:
+            events["gemm"][0].record(self.sa)
+        p.gemm_signal(self.A, self.B, self.buf, self.sig, e, trace=trace, stream=self.sa)
+        if events:
+            events["gemm"][1].record(self.sa)
+            events["consume"][0].record(self.sb)
+        p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status,
+                        timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups, stream=self.sb)
+        if events:
+            events["consume"][1].record(self.sb)
+            events["post"][0].record(self.sb)
+        p.reorder_post(self.recv, self.out, stream=self.sb)
+        if events:
+            events["post"][1].record(self.sb)
+        self.done_b.record(self.sb)
+        return e
+
+    def join(self):
+        """Make the current stream wait for both streams."""
+        cur = self.torch.cuda.current_stream(self.A.device)
+        ea, eb = self.torch.cuda.Event(), self.torch.cuda.Event()
+        ea.record(self.sa)
+        eb.record(self.sb)
+        cur.wait_event(ea)
+        cur.wait_event(eb)

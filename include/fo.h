@@ -1,0 +1,217 @@
+/*
+ * fo.h -- C ABI of the signaling GEMM with tile reordering for AMD MI355X (gfx950).
+ *
+ * The method is FlashOverlap's hot path, as the deep-dive page
+ * "FlashOverlap: 信号驱动计算通信重叠论文详解" (cited below as "deep-dive") and
+ * the summary page "Efficient and Adaptable Overlapping for Computation and
+ * Communication via Signaling and Reordering" (cited as "summary") describe it:
+ *
+ *   - one uninterrupted GEMM kernel (deep-dive, 核心设计 › 计算侧);
+ *   - its epilogue writes every finished tile through a mapping table into a
+ *     contiguous span per wave group (deep-dive 二、重排机制 › 解决方案),
+ *     then adds one to the group's entry of a counting table and raises the
+ *     group's signal when the entry reaches |G_j| (deep-dive 一、信号机制 ›
+ *     实现方法: 组级 Tile 计数; 五、CUTLASS 扩展实现 › 扩展主循环);
+ *   - a second kernel on another stream watches the signals and handles each
+ *     group's span as soon as it is signalled (deep-dive 五 › 专用监控内核;
+ *     核心设计 › 通信侧).  On one GPU it reduces the span with a second
+ *     buffer, a local stand-in for the group's collective;
+ *   - a post-communication kernel applies the inverse mapping and restores
+ *     row-major layout (deep-dive 二 › 解决方案; summary, Figure 5).
+ *
+ * Conventions shared by every call
+ *   - Return value: FO_OK (0) or a negative fo_status.  No call throws.
+ *   - Device pointers must be 16-byte aligned; host arrays have no alignment
+ *     requirement.  The caller allocates and owns every buffer it passes.
+ *   - Enqueue calls (fo_gemm_*, fo_consume_group, fo_reorder_*) are
+ *     asynchronous on the given HIP stream; they neither allocate nor copy
+ *     from the host nor synchronise.  Errors they return are detected on the
+ *     host before any launch; errors that arise on the device are written to
+ *     a caller-provided status word.
+ *   - Element types: FO_BF16 or FO_FP16 for A, B and every output buffer.
+ *     Accumulation is fp32; results are rounded to the element type,
+ *     round-to-nearest-even.
+ */
+#ifndef FO_H_
+#define FO_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fo_status {
+  FO_OK = 0,
+  FO_ERR_INVALID = -1,      /* bad argument: null or misaligned pointer, bad sizes, bad partition */
+  FO_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement (e.g. K % 64 != 0)  */
+  FO_ERR_HIP = -3,          /* a HIP runtime call failed                                       */
+  FO_ERR_NOMEM = -4,        /* host or device allocation failed at plan creation               */
+  FO_ERR_TIMEOUT = -5       /* device-side: the consumer waited longer than its time limit     */
+} fo_status;
+
+typedef enum fo_dtype { FO_BF16 = 0, FO_FP16 = 1 } fo_dtype;
+
+/* Reorder pattern per collective (deep-dive 二 › 不同通信原语的重排模式, Figure 6). */
+typedef enum fo_mode {
+  FO_MODE_TILE = 0,      /* AllReduce: whole tiles, row-major inside the tile             */
+  FO_MODE_SUBTILE = 1,   /* ReduceScatter: each tile cut into `ranks` row bands; a group's
+                            span holds band k of all its tiles as rank segment k           */
+  FO_MODE_SUBTOKEN = 2   /* All-to-All: each tile row goes to the bucket of its row's
+                            destination; a group's span holds `ranks` buckets              */
+} fo_mode;
+
+/* Plan flags. */
+#define FO_PLAN_HOST_ONLY 0x1u   /* build the tables on the host only; enqueue calls reject the plan */
+
+/*
+ * Problem description.  C[M, N] = A[M, K] . B^T where B is stored [N, K]
+ * (K contiguous, a linear layer's weight); A is row-major [M, K].  A grouped
+ * GEMM (MoE experts) stacks the problems' rows: A is [sum m_e, K], B holds
+ * num_problems consecutive [N, K] matrices, C is [sum m_e, N].
+ *
+ * Tiles are BM x BN; dispatch index b walks the tile grid in grouped-M
+ * order of width `swizzle` (bands of `swizzle` tile rows, column by column
+ * inside a band; deep-dive 一 › Block Swizzling 的影响), problem after
+ * problem.  Wave w holds dispatch indices [w*W, (w+1)*W) (deep-dive 一 ›
+ * 关键洞察: a wave is as many tiles as run at once); the GEMM runs a
+ * persistent grid of exactly W workgroups, so wave w is each workgroup's
+ * w-th tile.  T = ceil(NT / W).  The T waves are cut into P groups of
+ * waves_per_group[j] consecutive waves (deep-dive 一 › Wave Group 设计,
+ * 三 › 设计空间大小).  Slot s of the mapping table holds the tile with
+ * dispatch index s, so each group occupies consecutive slots and one
+ * contiguous span of the reordered buffer.  Edge tiles are packed.
+ */
+typedef struct fo_plan_desc {
+  int32_t num_problems;            /* >= 1                                                    */
+  const int64_t *m_per_problem;    /* host [num_problems]: rows of each problem (>= 0)        */
+  int64_t N, K;                    /* N % 8 == 0, K % 64 == 0, both > 0                        */
+  int32_t dtype;                   /* fo_dtype                                                */
+  int32_t BM, BN;                  /* tile: 256x128, 128x128 or 64x64; 0,0 = 256x128          */
+  int32_t swizzle;                 /* S >= 1; 0 = 4                                           */
+  int32_t wave_size;               /* W >= 1; 0 = the device's CU count (256 if host-only)    */
+  int32_t num_groups;              /* P; 0 = one wave per group (waves_per_group ignored)     */
+  const int32_t *waves_per_group;  /* host [P]: composition of T, every entry >= 1            */
+  int32_t mode;                    /* fo_mode                                                 */
+  int32_t ranks;                   /* R (SUBTILE: BM % R == 0, full tiles) or D (SUBTOKEN)    */
+  const int32_t *row_dest;         /* host [M], SUBTOKEN only: destination rank of each row   */
+  const int32_t *dispatch_order;   /* host [NT] or NULL: explicit b -> tile permutation       */
+  uint32_t flags;                  /* FO_PLAN_* bits                                          */
+} fo_plan_desc;
+
+typedef struct fo_plan fo_plan;
+
+typedef struct fo_plan_info {
+  int64_t M, N, K;
+  int32_t BM, BN, swizzle, wave_size;
+  int32_t NT;                      /* tiles                                                   */
+  int32_t T;                       /* waves                                                   */
+  int32_t P;                       /* groups                                                  */
+  int32_t num_units;               /* consumer work units (collective calls) over all groups  */
+  int32_t mode, ranks, dtype, num_problems;
+  int32_t device;                  /* HIP device the tables live on; -1 if host-only          */
+} fo_plan_info;
+
+/*
+ * Build a plan: tile grid, dispatch order, waves, groups, mapping table,
+ * thresholds |G_j| (in tiles), span and unit offsets, and the per-slot
+ * records the kernels read.  Unless FO_PLAN_HOST_ONLY is set the tables are
+ * uploaded once to the current HIP device; they are immutable afterwards, so
+ * a plan may be shared by streams and threads.  The plan must outlive all
+ * work enqueued with it.  *out is set only on FO_OK.
+ */
+int fo_plan_groups(const fo_plan_desc *desc, fo_plan **out);
+int fo_plan_destroy(fo_plan *plan);
+int fo_plan_info_get(const fo_plan *plan, fo_plan_info *out);
+
+/*
+ * Copy the plan's host tables into caller arrays (any may be NULL):
+ *   tile_of_slot[NT]  inverse mapping table: slot -> row-major tile index
+ *                     (tiles of problem e follow those of problems < e)
+ *   slot_of_tile[NT]  mapping table: tile -> slot
+ *   group_of_slot[NT] group j of each slot
+ *   group_tiles[P]    |G_j| in tiles: the counting table's target per group
+ *   span_off[P+1]     element offset of each group's contiguous span
+ */
+int fo_plan_tables(const fo_plan *plan, int32_t *tile_of_slot, int32_t *slot_of_tile,
+                   int32_t *group_of_slot, int32_t *group_tiles, int64_t *span_off);
+
+/*
+ * Consumer work units: unit_off[num_units+1] element bounds (unit u is
+ * [unit_off[u], unit_off[u+1])) and group_unit[P+1] (group j owns units
+ * [group_unit[j], group_unit[j+1])).  TILE: one unit per group; SUBTILE: R
+ * rank segments per group; SUBTOKEN: D destination buckets per group.
+ */
+int fo_plan_units(const fo_plan *plan, int64_t *unit_off, int32_t *group_unit);
+
+/*
+ * Host-side check of the layout the kernels use: off[m * N + n] receives
+ * the reordered offset of output element (m, n), computed from the same
+ * per-slot records that the device reads.  off has M * N entries.
+ */
+int fo_plan_offsets(const fo_plan *plan, int64_t *off);
+
+/*
+ * Signaling GEMM (deep-dive 五 › 扩展主循环 and Epilogue 集成): C = A . B^T
+ * with every finished tile stored through the mapping table into
+ * `reorder_buf` (M*N elements, the contiguous per-group spans), followed by
+ * a release of the tile's stores to device scope, one atomic increment of
+ * cnt[group], and -- by the tile that brings cnt[group] to epoch*|G_group|
+ * -- a release store flag[group] = epoch.
+ *
+ * sig: device uint32[2*P] = cnt[P] followed by flag[P]; zero it once before
+ *      the first epoch.  Epochs start at 1 and increase by 1 per launch on
+ *      the same sig, so no reset is needed between launches; after epoch e,
+ *      cnt[j] == e*|G_j|.  epoch * max|G_j| must fit in 32 bits.
+ * trace: NULL, or device uint64[2*NT + P]: for slot s, trace[2s] = wall
+ *      clock at the tile's signal, trace[2s+1] = (workgroup << 32) | the
+ *      counter value before the increment; trace[2NT + j] += 1 when group j
+ *      fires.  Zero it before the launch.
+ */
+int fo_gemm_signal(const fo_plan *plan, const void *A, const void *B, void *reorder_buf,
+                   uint32_t *sig, uint32_t epoch, uint64_t *trace, hipStream_t stream);
+
+/*
+ * The same GEMM main loop with a plain row-major epilogue and no signaling:
+ * C[M, N] row-major.  Reference for the interference check.
+ */
+int fo_gemm_plain(const fo_plan *plan, const void *A, const void *B, void *C, hipStream_t stream);
+
+/*
+ * Consumer: for groups g = g_begin .. g_end-1 in order, wait on the device
+ * until flag[g] >= epoch, then for every unit of g compute
+ *   recv[u] = round(float(send[u]) + float(peer[u]))   (element type, RNE)
+ * over the unit's elements.  send, peer, recv are flat M*N buffers in the
+ * reordered layout; recv may equal send.  This stands in for the group's
+ * collective call on the contiguous span (deep-dive 二 › (1) code box;
+ * 五 › 专用监控内核).
+ *
+ * num_workgroups: persistent grid size (0 = the device's CU count).
+ * timeout_us: upper bound on any one wait (0 = 2 s).  A workgroup that
+ *      waits longer stores FO_ERR_TIMEOUT into *dev_status (if it was still
+ *      0) and every workgroup then stops; later spans are left untouched.
+ * dev_status: device int32, caller zeroes it; read it after synchronising.
+ * The GEMM that raises the flags must run on a different stream; the two
+ * are linked only through sig.  The consumer occupies few resources so
+ * that it can stay resident beside the GEMM.
+ */
+int fo_consume_group(const fo_plan *plan, const void *send, const void *peer, void *recv,
+                     const uint32_t *sig, uint32_t epoch, int32_t g_begin, int32_t g_end,
+                     int32_t *dev_status, uint64_t timeout_us, int32_t num_workgroups,
+                     hipStream_t stream);
+
+/* Post-communication reordering: out[m*N + n] = reordered[off(m, n)] (inverse mapping). */
+int fo_reorder_post(const fo_plan *plan, const void *reordered, void *out, hipStream_t stream);
+
+/* Pre-communication reordering as a separate pass: reordered[off(m, n)] = in[m*N + n]. */
+int fo_reorder_pre(const fo_plan *plan, const void *in, void *reordered, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *fo_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FO_H_ */

@@ -1,0 +1,57 @@
+"""Helpers for the GPU tests: device buffers from seeded host arrays, tolerance checks.
+
+Inputs come from ``workloads`` (seeded, synthetic); expected values come from
+``oracle`` applied to the same host arrays.  Nothing here computes any part of
+the method.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+
+def say(msg: str):
+    """Name the case before a GPU step, flushed, so a failure can be located."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).to("cuda")
+
+
+def to_host(t) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def empty16(n: int, fill: int = 0x7FC0):
+    """A device buffer of n 16-bit elements pre-filled with a marker pattern (a NaN)."""
+    import torch
+    return torch.full((n,), np.int16(np.uint16(fill).view(np.int16)), dtype=torch.int16, device="cuda")
+
+
+def zeros_i32(n: int):
+    import torch
+    return torch.zeros(n, dtype=torch.int32, device="cuda")
+
+
+def tol_check(gpu_bits, ref_f64, dtype: str, what: str):
+    """|gpu - oracle| <= 1e-2 * max(1, |oracle|) element by element; returns the diagnostic ratio."""
+    g = oracle.decode_bits(gpu_bits, dtype)
+    r = np.asarray(ref_f64, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values in the GPU result"
+    err = np.abs(g - r)
+    bound = 1e-2 * np.maximum(1.0, np.abs(r))
+    bad = err > bound
+    if bad.any():
+        i = int(np.argmax(bad.ravel()))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; first at flat index {i}: "
+                             f"gpu {g.ravel()[i]!r} oracle {r.ravel()[i]!r}")
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    return float(err.max() / rms) if rms > 0 and err.size else 0.0

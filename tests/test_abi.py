@@ -1,0 +1,71 @@
+"""The C-ABI library loads, exports every symbol include/fo.h declares, and
+rejects bad arguments with the documented codes -- all without a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+fo = pytest.importorskip("gemm_tile_signaling_amd")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "fo.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fo_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"fo_plan_groups", "fo_gemm_signal", "fo_consume_group", "fo_reorder_post"} <= set(names)
+    L = ctypes.CDLL(fo.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert fo.status_string(0) == "ok"
+    for c in (-1, -2, -3, -4, -5):
+        assert fo.status_string(c) not in ("ok", "unknown status")
+    assert fo.status_string(-99) == "unknown status"
+
+
+def _code(fn):
+    with pytest.raises(fo.FoError) as e:
+        fn()
+    return e.value.code
+
+
+def test_plan_argument_errors():
+    P = fo.Plan
+    assert _code(lambda: P(256, 256, 256, composition=(1, 2), BM=64, BN=64, wave_size=4, host_only=True)) == -1
+    assert _code(lambda: P(256, 256, 256, composition=(0, 4), BM=64, BN=64, wave_size=4, host_only=True)) == -1
+    assert _code(lambda: P(256, 250, 256, host_only=True)) == -1                    # N % 8
+    assert _code(lambda: P(256, 256, 200, host_only=True)) == -2                    # K % 64
+    assert _code(lambda: P(256, 256, 256, BM=32, BN=32, host_only=True)) == -2      # tile shape
+    assert _code(lambda: P(250, 256, 256, BM=64, BN=64, mode="subtile", ranks=4, host_only=True)) == -1
+    assert _code(lambda: P(256, 256, 256, BM=64, BN=64, mode="subtile", ranks=3, host_only=True)) == -1
+    assert _code(lambda: P(4, 64, 64, BM=64, BN=64, mode="subtoken", ranks=2, row_dest=[0, 1, 2, 0],
+                           host_only=True)) == -1
+    assert _code(lambda: P(128, 128, 64, BM=64, BN=64, dispatch_order=[0, 0, 1, 2], host_only=True)) == -1
+    assert _code(lambda: P([-1], 64, 64, host_only=True)) == -1
+
+
+def test_enqueue_on_host_only_plan_is_rejected():
+    p = fo.Plan(256, 256, 256, "fp16", BM=64, BN=64, swizzle=2, wave_size=4, composition=(1, 2, 1), host_only=True)
+    # addresses are never dereferenced: the host-only plan is refused first
+    assert _code(lambda: p.gemm_signal(16, 16, 16, 16, 1, stream=0)) == -1
+    assert _code(lambda: p.gemm_plain(16, 16, 16, stream=0)) == -1
+    assert _code(lambda: p.consume_group(16, 16, 16, 16, 1, 16, stream=0)) == -1
+    assert _code(lambda: p.reorder_post(16, 16, stream=0)) == -1
+    assert _code(lambda: p.reorder_pre(16, 16, stream=0)) == -1
+    assert p.info["device"] == -1
+
+
+def test_default_plan_parameters():
+    p = fo.Plan(2048, 8192, 8192, host_only=True)
+    assert (p.BM, p.BN, p.S, p.W) == (256, 128, 4, 256)
+    assert p.NT == 512 and p.T == 2 and p.P == 2

@@ -1,0 +1,242 @@
+"""GPU parity of each kernel against the oracle, on seeded inputs spanning several tiles and ragged edges.
+
+Bit-exact: both reorders, the consumer's add, the counting table, flags,
+tickets and fire counts, and the GEMM on ternary inputs (exact integers).
+Within |gpu - oracle| <= 1e-2 * max(1, |oracle|): the GEMM on real-valued
+inputs.  All calls go through the C ABI (the ctypes binding).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.layout import element_offsets, group_spans
+from oracle.tiles import make_plan
+from tests.gpu_util import empty16, say, to_dev, to_host, tol_check, zeros_i32
+from workloads import draw, random_bits, to_bits
+
+pytestmark = pytest.mark.gpu
+
+fo = pytest.importorskip("gemm_tile_signaling_amd")
+torch = pytest.importorskip("torch")
+
+
+def _rng_dest(M, D, seed):
+    return np.random.Generator(np.random.PCG64(seed)).integers(0, D, size=M)
+
+
+# (name, m_per_problem, N, K, dtype, BM, BN, S, W, composition, mode, ranks)
+PLANS = [
+    ("tiny_fp16", [256], 256, 256, "fp16", 64, 64, 2, 4, (1, 2, 1), "tile", 1),
+    ("ragged_64", [250], 200, 128, "bf16", 64, 64, 3, 5, None, "tile", 1),
+    ("ragged_128", [1000], 264, 192, "bf16", 128, 128, 3, 7, None, "tile", 1),
+    ("ragged_256", [513], 384, 320, "bf16", 256, 128, 4, 3, (1, 1, 1), "tile", 1),
+    ("subtile_r4", [1024], 256, 128, "bf16", 256, 128, 2, 3, None, "subtile", 4),
+    ("subtile_r2_fp16", [256], 192, 64, "fp16", 64, 64, 2, 4, (2, 1), "subtile", 2),
+    ("subtoken_d4", [70, 0, 130, 64], 192, 128, "bf16", 128, 128, 2, 3, None, "subtoken", 4),
+    ("subtoken_d8_256", [300, 257, 1], 256, 64, "bf16", 256, 128, 1, 2, None, "subtoken", 8),
+]
+
+
+def _plans(entry):
+    name, m, N, K, dt, BM, BN, S, W, comp, mode, R = entry
+    dest = _rng_dest(sum(m), R, 5) if mode == "subtoken" else None
+    o = make_plan(m, N, BM=BM, BN=BN, S=S, W=W, composition=comp, mode=mode, ranks=R, row_dest=dest)
+    p = fo.Plan(m, N, K, dt, BM=BM, BN=BN, swizzle=S, wave_size=W, composition=comp, mode=mode, ranks=R,
+                row_dest=dest)
+    return o, p
+
+
+def _inputs(entry, dist=None, seed=100):
+    name, m, N, K, dt, *_ = entry
+    M = sum(m)
+    if dist is None:
+        dist = ("normal", 0.5) if dt == "bf16" else ("uniform", -1.0, 1.0)
+    A = to_bits(draw(seed + 1, (M, K), dist), dt)
+    B = [to_bits(draw(seed + 2 + e, (N, K), dist), dt) for e in range(len(m))]
+    peer = to_bits(draw(seed + 50, (M * N,), dist), dt)
+    return A, B, peer
+
+
+def _stack(B):
+    return np.concatenate([b.reshape(-1) for b in B])
+
+
+# --------------------------------------------------------------------------- reorders
+
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_reorder_pre_post_bit_exact(entry):
+    o, p = _plans(entry)
+    off = element_offsets(o)
+    X = random_bits(7, o.M * o.N, entry[4])
+    Y = random_bits(8, o.M * o.N, entry[4])
+    want_pre = oracle.pre_reorder(X.reshape(o.M, o.N), off)
+    want_post = oracle.post_reorder(Y, off).ravel()
+    say(f"reorder {entry[0]} M={o.M} N={o.N} NT={o.NT}")
+    dX, dY = to_dev(X), to_dev(Y)
+    r1, r2 = empty16(o.M * o.N), empty16(o.M * o.N)
+    p.reorder_pre(dX, r1)
+    p.reorder_post(dY, r2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(r1), want_pre)
+    assert np.array_equal(to_host(r2), want_post)
+
+
+# --------------------------------------------------------------------------- consumer
+
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_consumer_all_groups_bit_exact(entry):
+    o, p = _plans(entry)
+    dt = entry[4]
+    send = random_bits(11, o.M * o.N, dt)
+    peer = random_bits(12, o.M * o.N, dt)
+    want = oracle.consume_add(send, peer, dt)
+    say(f"consumer {entry[0]} P={o.P} units={p.num_units}")
+    sig = zeros_i32(2 * p.P)
+    sig[p.P:] = 3                      # every group already signalled at epoch 3
+    status = zeros_i32(1)
+    dsend, dpeer = to_dev(send), to_dev(peer)
+    recv = empty16(o.M * o.N)
+    p.consume_group(dsend, dpeer, recv, sig, 3, status, num_workgroups=7)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(to_host(recv), want)
+    # in place: recv aliases send
+    p.consume_group(dsend, dpeer, dsend, sig, 3, status)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dsend), want)
+
+
+def test_consumer_times_out_on_unsignalled_group_and_leaves_it_untouched():
+    entry = PLANS[0]
+    o, p = _plans(entry)
+    dt = entry[4]
+    send = random_bits(21, o.M * o.N, dt)
+    peer = random_bits(22, o.M * o.N, dt)
+    want = oracle.consume_add(send, peer, dt)
+    spans = group_spans(o)
+    say("consumer time-out: group 2 never signalled, 20 ms limit")
+    sig = zeros_i32(2 * p.P)
+    sig[p.P + 0] = 1
+    sig[p.P + 1] = 1                   # group 2 stays at 0: the host never raises it
+    status = zeros_i32(1)
+    recv = empty16(o.M * o.N)
+    p.consume_group(to_dev(send), to_dev(peer), recv, sig, 1, status, timeout_us=20000, num_workgroups=4)
+    torch.cuda.synchronize()
+    assert int(status.item()) == fo.FO_ERR_TIMEOUT
+    got = to_host(recv)
+    assert np.array_equal(got[:spans[2]], want[:spans[2]])
+    assert np.all(got[spans[2]:] == 0x7FC0)
+
+
+def test_consumer_group_range():
+    entry = PLANS[1]
+    o, p = _plans(entry)
+    send = random_bits(31, o.M * o.N, "bf16")
+    peer = random_bits(32, o.M * o.N, "bf16")
+    want = oracle.consume_add(send, peer, "bf16")
+    spans = group_spans(o)
+    say("consumer groups [1, 3)")
+    sig = zeros_i32(2 * p.P)
+    sig[p.P:] = 1
+    status = zeros_i32(1)
+    recv = empty16(o.M * o.N)
+    p.consume_group(to_dev(send), to_dev(peer), recv, sig, 1, status, g_begin=1, g_end=3)
+    torch.cuda.synchronize()
+    got = to_host(recv)
+    assert np.array_equal(got[spans[1]:spans[3]], want[spans[1]:spans[3]])
+    assert np.all(got[:spans[1]] == 0x7FC0) and np.all(got[spans[3]:] == 0x7FC0)
+
+
+# --------------------------------------------------------------------------- GEMM
+
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_gemm_plain_within_tolerance(entry):
+    o, p = _plans(entry)
+    dt = entry[4]
+    A, B, _ = _inputs(entry)
+    r = oracle.run_pipeline(A, B, np.zeros(o.M * o.N, np.uint16), o, dt)
+    say(f"gemm_plain {entry[0]} M={o.M} N={o.N} K={p.K} tile={p.BM}x{p.BN}")
+    C = empty16(o.M * o.N)
+    p.gemm_plain(to_dev(A), to_dev(_stack(B)), C)
+    torch.cuda.synchronize()
+    ratio = tol_check(to_host(C).reshape(o.M, o.N), r["C64"], dt, "C")
+    assert ratio < 0.05, ratio           # diagnostic: a wrong k-slice or operand would be O(1)
+
+
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_gemm_ternary_bit_exact(entry):
+    o, p = _plans(entry)
+    dt = entry[4]
+    if p.K > 256:
+        pytest.skip("ternary products are exact in 16 bits only for K <= 256")
+    A, B, _ = _inputs(entry, dist=("ternary",))
+    r = oracle.run_pipeline(A, B, np.zeros(o.M * o.N, np.uint16), o, dt)
+    say(f"gemm ternary {entry[0]}")
+    C = empty16(o.M * o.N)
+    buf = empty16(o.M * o.N)
+    sig = zeros_i32(2 * p.P)
+    dA, dB = to_dev(A), to_dev(_stack(B))
+    p.gemm_plain(dA, dB, C)
+    p.gemm_signal(dA, dB, buf, sig, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(C), r["C"].ravel())
+    assert np.array_equal(to_host(buf), r["send"])
+
+
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_gemm_signal_tables_and_layout(entry):
+    o, p = _plans(entry)
+    dt = entry[4]
+    A, B, _ = _inputs(entry, seed=300)
+    r = oracle.run_pipeline(A, B, np.zeros(o.M * o.N, np.uint16), o, dt)
+    say(f"gemm_signal {entry[0]} P={o.P} thresholds={o.group_tiles}")
+    dA, dB = to_dev(A), to_dev(_stack(B))
+    C = empty16(o.M * o.N)
+    buf = empty16(o.M * o.N)
+    back = empty16(o.M * o.N)
+    sig = zeros_i32(2 * p.P)
+    trace = torch.zeros(2 * p.NT + p.P, dtype=torch.int64, device="cuda")
+    p.gemm_plain(dA, dB, C)
+    for epoch in (1, 2, 3):
+        trace.zero_()
+        p.gemm_signal(dA, dB, buf, sig, epoch, trace=trace)
+        torch.cuda.synchronize()
+        s = sig.cpu().numpy()
+        assert s[:p.P].tolist() == [epoch * g for g in o.group_tiles]          # counting table
+        assert s[p.P:].tolist() == [epoch] * p.P                               # every group signalled
+        tr = trace.cpu().numpy().view(np.uint64)
+        tickets = (tr[1:2 * p.NT:2] & 0xFFFFFFFF).astype(np.int64)
+        for j in range(p.P):
+            got = np.sort(tickets[np.array(o.group_of_b) == j])
+            assert got.tolist() == list(range((epoch - 1) * o.group_tiles[j], epoch * o.group_tiles[j]))
+        assert tr[2 * p.NT:].tolist() == [1] * p.P                             # each group fired once
+        wg = (tr[1:2 * p.NT:2] >> 32).astype(np.int64)
+        assert np.all(wg < p.W)
+    # reordered layout: within tolerance of the oracle's pre-reordered C ...
+    tol_check(to_host(buf), oracle.pre_reorder(r["C64"], r["off"]), dt, "reorder_buf")
+    # ... and bit-identical to the plain GEMM once reordered back
+    p.reorder_post(buf, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(back), to_host(C))
+
+
+def test_gemm_each_workgroup_runs_its_wave_slot():
+    """With W = 4 on the tiny shape, workgroup g runs dispatch indices g, g+4, g+8, g+12."""
+    entry = PLANS[0]
+    o, p = _plans(entry)
+    A, B, _ = _inputs(entry)
+    say("gemm_signal wave placement W=4")
+    sig = zeros_i32(2 * p.P)
+    trace = torch.zeros(2 * p.NT + p.P, dtype=torch.int64, device="cuda")
+    buf = empty16(o.M * o.N)
+    p.gemm_signal(to_dev(A), to_dev(_stack(B)), buf, sig, 1, trace=trace)
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy().view(np.uint64)
+    wg = (tr[1:2 * p.NT:2] >> 32).astype(np.int64)
+    assert wg.tolist() == [b % 4 for b in range(p.NT)]
+    # per workgroup, its tiles signal in dispatch order
+    ts = tr[0:2 * p.NT:2].astype(np.int64)
+    for g in range(4):
+        t = ts[g::4]
+        assert np.all(np.diff(t) >= 0)

@@ -1,0 +1,83 @@
+"""GPU parity of the whole path (signaling GEMM on stream A, consumer and
+post-reorder on stream B) against the oracle's pipeline, small shapes.
+
+Real-valued inputs: the final row-major output within 1e-2 * max(1, |oracle|).
+Ternary inputs: bit-exact.  Several passes back to back with increasing epochs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.tiles import make_plan
+from tests.gpu_util import say, to_dev, to_host, tol_check
+from tests.test_gpu_kernels import PLANS, _inputs, _plans, _stack
+
+pytestmark = pytest.mark.gpu
+
+fo = pytest.importorskip("gemm_tile_signaling_amd")
+torch = pytest.importorskip("torch")
+from gemm_tile_signaling_amd.pipeline import Pipeline  # noqa: E402
+
+
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_pipeline_matches_oracle(entry, in_place):
+    o, p = _plans(entry)
+    dt = entry[4]
+    A, B, peer = _inputs(entry, seed=500)
+    r = oracle.run_pipeline(A, B, peer, o, dt)
+    C = oracle.decode_bits(r["C"], dt)
+    want_out = oracle.round_to_dtype(C + oracle.decode_bits(peer, dt)[r["off"]], dt)   # definition, row-major
+    say(f"pipeline {entry[0]} in_place={in_place}")
+    pipe = Pipeline(p, to_dev(A), to_dev(_stack(B)), to_dev(peer), in_place=in_place)
+    for _ in range(3):
+        pipe.step()
+    pipe.join()
+    torch.cuda.synchronize()
+    assert int(pipe.status.item()) == 0
+    s = pipe.sig.cpu().numpy()
+    assert s[:p.P].tolist() == [3 * g for g in o.group_tiles]
+    assert s[p.P:].tolist() == [3] * p.P
+    out = to_host(pipe.out).reshape(o.M, o.N)
+    tol_check(out, want_out, dt, "out")
+    # the oracle's own end-to-end result agrees with its definition
+    assert np.array_equal(r["out"], oracle.encode_bits(want_out, dt))
+
+
+@pytest.mark.parametrize("entry", [e for e in PLANS if e[3] <= 256], ids=[e[0] for e in PLANS if e[3] <= 256])
+def test_pipeline_ternary_bit_exact(entry):
+    o, p = _plans(entry)
+    dt = entry[4]
+    A, B, peer = _inputs(entry, dist=("ternary",), seed=600)
+    r = oracle.run_pipeline(A, B, peer, o, dt)
+    say(f"pipeline ternary {entry[0]}")
+    pipe = Pipeline(p, to_dev(A), to_dev(_stack(B)), to_dev(peer))
+    pipe.step()
+    pipe.step()
+    pipe.join()
+    torch.cuda.synchronize()
+    assert int(pipe.status.item()) == 0
+    assert np.array_equal(to_host(pipe.recv), r["recv"])
+    assert np.array_equal(to_host(pipe.out), r["out"].ravel())
+
+
+@pytest.mark.parametrize("comp", [(1, 1, 1, 1), (1, 2, 1), (2, 2), (4,), (3, 1), (1, 3)])
+def test_tiny_workload_every_partition_kind(comp):
+    """The fp16 worked-example-sized GEMM under several wave-group partitions."""
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["tiny"]
+    A, B, peer, m_per, _ = make_inputs(w)
+    o = make_plan(m_per, w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=comp)
+    p = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp)
+    r = oracle.run_pipeline(A, B, peer, o, w.dtype)
+    say(f"tiny partition {comp}")
+    pipe = Pipeline(p, to_dev(A), to_dev(B[0]), to_dev(peer))
+    pipe.step()
+    pipe.join()
+    torch.cuda.synchronize()
+    assert int(pipe.status.item()) == 0
+    assert pipe.sig.cpu().numpy()[:p.P].tolist() == o.group_tiles
+    want = oracle.round_to_dtype(oracle.decode_bits(r["C"], w.dtype) + oracle.decode_bits(peer, w.dtype)[r["off"]],
+                                 w.dtype)
+    tol_check(to_host(pipe.out).reshape(o.M, o.N), want, w.dtype, "out")
