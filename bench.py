@@ -41,7 +41,6 @@ def _args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="profiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle's CPU sample (0 = auto)")
     return ap.parse_args()
 
 
@@ -67,8 +66,13 @@ def _time_kernel(torch, launch, stream, n, scratch=None):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, rows):
-    """The oracle pipeline (fp64 GEMM, pre-reorder, consumer, post-reorder) on the first ``rows`` rows."""
+def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, min_seconds=10.0):
+    """The oracle pipeline (fp64 GEMM, pre-reorder, consumer, post-reorder) on the host cores.
+
+    One pass over the whole workload takes about a second on a 16-core host,
+    so the bounded sample is the full workload, repeated until about
+    ``min_seconds`` of CPU work have been timed.
+    """
     import oracle
     from oracle.tiles import make_plan
     try:
@@ -76,15 +80,19 @@ def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, rows):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    rows = min(rows, w.M)
-    T_s = -(-(-(-rows // w.BM) * -(-w.N // w.BN)) // w.W)
-    plan = make_plan([rows], w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=(T_s,), mode="tile")
-    t0 = time.perf_counter()
-    oracle.run_pipeline(A[:rows], B, peer[: rows * w.N], plan, w.dtype)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * w.N * w.K
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"first {rows} of {w.M} rows (M={rows}, N={w.N}, K={w.K}), one group; {dt:.2f} s")
+    plan = make_plan(m_per, w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=comp, mode=w.mode, ranks=w.ranks,
+                     row_dest=row_dest)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run_pipeline(A, B, peer, plan, w.dtype)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 50:
+            break
+    flops = 2.0 * w.M * w.N * w.K * reps
+    return dict(value=round(flops / dt / 1e12, 4), unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"full workload (M={w.M}, N={w.N}, K={w.K}, groups {tuple(comp)}) x {reps} passes, "
+                       f"{dt:.1f} s")
 
 
 def main():
@@ -134,6 +142,21 @@ def main():
     best = min(results, key=lambda r: r["step_ms"])
     plan, pipe = best["plan"], best["pipe"]
 
+    # one traced pass: device wall-clock stamps of every tile's signal and of each consumer wait
+    gtr = torch.zeros(2 * plan.NT + plan.P, dtype=torch.int64, device=dev)
+    ctr = torch.zeros(plan.P, dtype=torch.int64, device=dev)
+    pipe.step(trace=gtr, consumer_trace=ctr)
+    pipe.join()
+    torch.cuda.synchronize()
+    g = gtr.cpu().numpy().view(np.uint64).astype(np.int64)
+    c = ctr.cpu().numpy().view(np.uint64).astype(np.int64)
+    tick_us = 1e3 / plan.info["clock_khz"]
+    grp = np.array(plan.tables()["group_of_slot"])
+    t_sig = g[0:2 * plan.NT:2]
+    last = np.array([t_sig[grp == j].max() for j in range(plan.P)])
+    signal_to_consume_us = [round(float(x) * tick_us, 2) for x in (c - last)]
+    first_consume_before_gemm_end_us = round(float(last[-1] - c[0]) * tick_us, 2)
+
     # kernels alone (same plan), each timed with HIP events on its own stream
     s = torch.cuda.Stream(device=dev)
     n_alone = max(10, min(a.steps, 50))
@@ -182,14 +205,15 @@ def main():
         "post_reorder_alone_gbps": round(post_gbps, 1),
         "consumer_frac_hbm": round(consume_gbps / PEAK_HBM_GBPS, 4),
         "post_reorder_frac_hbm": round(post_gbps / PEAK_HBM_GBPS, 4),
+        "signal_to_consume_us": signal_to_consume_us,
+        "first_group_consumed_before_gemm_end_us": first_consume_before_gemm_end_us,
         "partitions": [{"groups": list(r["comp"]), "step_ms": round(r["step_ms"], 4),
                         "gemm_ms": round(r["gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
                         "post_ms": round(r["post_ms"], 4)} for r in results],
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:
-        rows = a.cpu_rows or 512
-        line["cpu_baseline"] = cpu_baseline(w, A, B, peer, m_per, row_dest, comps[0], rows)
+        line["cpu_baseline"] = cpu_baseline(w, A, B, peer, m_per, row_dest, best["comp"])
     print(json.dumps(line), flush=True)
 
 

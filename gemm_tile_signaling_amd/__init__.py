@@ -21,7 +21,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-__all__ = ["Plan", "FoError", "lib", "LIB_PATH", "status_string",
+__all__ = ["Plan", "FoError", "lib", "LIB_PATH", "status_string", "stream_create", "stream_destroy",
            "FO_OK", "FO_ERR_INVALID", "FO_ERR_UNSUPPORTED", "FO_ERR_HIP", "FO_ERR_NOMEM", "FO_ERR_TIMEOUT"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
@@ -52,7 +52,7 @@ class _Desc(C.Structure):
 class _Info(C.Structure):
     _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64)] + [
         (n, C.c_int32) for n in ("BM", "BN", "swizzle", "wave_size", "NT", "T", "P", "num_units",
-                                 "mode", "ranks", "dtype", "num_problems", "device")]
+                                 "mode", "ranks", "dtype", "num_problems", "device", "clock_khz")]
 
 
 _lib = None
@@ -76,7 +76,9 @@ def lib() -> C.CDLL:
             "fo_plan_offsets": [vp, vp],
             "fo_gemm_signal": [vp, vp, vp, vp, vp, u32, vp, vp],
             "fo_gemm_plain": [vp, vp, vp, vp, vp],
-            "fo_consume_group": [vp, vp, vp, vp, vp, u32, i32, i32, vp, u64, i32, vp],
+            "fo_consume_group": [vp, vp, vp, vp, vp, u32, i32, i32, vp, u64, i32, vp, vp],
+            "fo_stream_create": [C.POINTER(vp)],
+            "fo_stream_destroy": [vp],
             "fo_reorder_post": [vp, vp, vp, vp],
             "fo_reorder_pre": [vp, vp, vp, vp],
         }
@@ -132,6 +134,18 @@ def _stream(s) -> int:
     if isinstance(s, int):
         return s
     return int(s.cuda_stream)
+
+
+def stream_create():
+    """A HIP stream with a hardware queue of its own (``fo_stream_create``), as a torch stream."""
+    import torch
+    h = C.c_void_p()
+    _check(lib().fo_stream_create(C.byref(h)), "fo_stream_create")
+    return torch.cuda.ExternalStream(h.value)
+
+
+def stream_destroy(s):
+    _check(lib().fo_stream_destroy(int(s.cuda_stream)), "fo_stream_destroy")
 
 
 class Plan:
@@ -215,14 +229,14 @@ class Plan:
             _ptr(Cout, numel=self.mn, itemsize=2, name="C"), _stream(stream)), "fo_gemm_plain")
 
     def consume_group(self, send, peer, recv, sig, epoch: int, status, g_begin: int = 0, g_end: Optional[int] = None,
-                      timeout_us: int = 0, num_workgroups: int = 0, stream=None):
+                      timeout_us: int = 0, num_workgroups: int = 0, trace=None, stream=None):
         g_end = self.P if g_end is None else g_end
         _check(lib().fo_consume_group(
             self._h, _ptr(send, numel=self.mn, itemsize=2, name="send"),
             _ptr(peer, numel=self.mn, itemsize=2, name="peer"), _ptr(recv, numel=self.mn, itemsize=2, name="recv"),
             _ptr(sig, numel=2 * self.P, itemsize=4, name="sig"), int(epoch), int(g_begin), int(g_end),
             _ptr(status, numel=1, itemsize=4, name="status"), int(timeout_us), int(num_workgroups),
-            _stream(stream)), "fo_consume_group")
+            _ptr(trace, numel=self.P, itemsize=8, name="trace"), _stream(stream)), "fo_consume_group")
 
     def reorder_post(self, reordered, out, stream=None):
         _check(lib().fo_reorder_post(self._h, _ptr(reordered, numel=self.mn, itemsize=2, name="reordered"),

@@ -1,6 +1,9 @@
 // Enqueue calls of the C ABI: argument checks on the host, then the launchers.
 // Nothing here allocates, copies from the host or synchronises.
 #include <cstdint>
+#include <vector>
+
+#include <hip/hip_ext.h>
 
 #include "fo_internal.h"
 
@@ -39,7 +42,7 @@ int fo_gemm_plain(const fo_plan *p, const void *A, const void *B, void *C, hipSt
 
 int fo_consume_group(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
                      uint32_t epoch, int32_t g_begin, int32_t g_end, int32_t *dev_status, uint64_t timeout_us,
-                     int32_t num_workgroups, hipStream_t stream) {
+                     int32_t num_workgroups, uint64_t *trace, hipStream_t stream) {
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (g_begin < 0 || g_end > p->P || g_begin > g_end) return FO_ERR_INVALID;
   if (g_begin == g_end) return FO_OK;
@@ -50,8 +53,9 @@ int fo_consume_group(const fo_plan *p, const void *send, const void *peer, void 
   const int32_t grid = num_workgroups ? num_workgroups : (p->num_cus > 0 ? p->num_cus : 256);
   const uint64_t us = timeout_us ? timeout_us : 2000000ull;
   if (us > (1ull << 40)) return FO_ERR_INVALID;
+  if (trace && (reinterpret_cast<uintptr_t>(trace) & 7u)) return FO_ERR_INVALID;
   return fo::launch_consume(p, send, peer, recv, sig, epoch, g_begin, g_end, dev_status, us * p->ticks_per_us, grid,
-                            stream);
+                            trace, stream);
 }
 
 int fo_reorder_post(const fo_plan *p, const void *reordered, void *out, hipStream_t stream) {
@@ -64,6 +68,26 @@ int fo_reorder_pre(const fo_plan *p, const void *in, void *reordered, hipStream_
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (!buf_ok(p, in) || !buf_ok(p, reordered)) return FO_ERR_INVALID;
   return fo::launch_reorder(p, in, reordered, false, stream);
+}
+
+int fo_stream_create(hipStream_t *out) {
+  if (!out) return FO_ERR_INVALID;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return FO_ERR_HIP;
+  // every CU enabled; a masked stream is given a hardware queue of its own
+  std::vector<uint32_t> mask((cus + 31) / 32, 0xFFFFFFFFu);
+  if (cus % 32) mask.back() = (1u << (cus % 32)) - 1u;
+  hipStream_t s = nullptr;
+  if (hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data()) != hipSuccess) return FO_ERR_HIP;
+  *out = s;
+  return FO_OK;
+}
+
+int fo_stream_destroy(hipStream_t stream) {
+  if (!stream) return FO_ERR_INVALID;
+  return hipStreamDestroy(stream) == hipSuccess ? FO_OK : FO_ERR_HIP;
 }
 
 }  // extern "C"

@@ -36,6 +36,7 @@ struct ConsumeParams {
   const int64_t *unit_off;
   const int32_t *group_unit;
   int32_t *status;
+  uint64_t *trace;         // NULL or [P]: wall clock when workgroup 0's wait for a group ended
   uint64_t timeout_ticks;
   uint32_t epoch;
   int32_t g_begin, g_end;
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
         }
       }
       s_go = go;
+      if (go && p.trace && blockIdx.x == 0) p.trace[g] = wall_clock64();
     }
     __syncthreads();
     const int go = s_go;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
 
 int launch_consume(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
                    uint32_t epoch, int32_t g_begin, int32_t g_end, int32_t *status, uint64_t timeout_ticks,
-                   int32_t grid, hipStream_t s) {
+                   int32_t grid, uint64_t *trace, hipStream_t s) {
   if (g_begin >= g_end) return FO_OK;
   ConsumeParams cp{};
   cp.send = static_cast<const uint16_t *>(send);
@@ -129,6 +131,7 @@ int launch_consume(const fo_plan *p, const void *send, const void *peer, void *r
   cp.unit_off = p->d_unit_off;
   cp.group_unit = p->d_group_unit;
   cp.status = status;
+  cp.trace = trace;
   cp.timeout_ticks = timeout_ticks;
   cp.epoch = epoch;
   cp.g_begin = g_begin;

@@ -30,9 +30,10 @@
 //   * Epilogue: accumulators -> 16-bit -> LDS staging tile; every valid row's
 //     destination offset (row-major, banded or subtoken layout) is computed
 //     once into LDS; then 16-byte coalesced stores.  With signaling on, each
-//     wave releases its stores to device scope, the workgroup meets at a
-//     barrier, and one lane increments cnt[group]; the lane that brings it to
-//     epoch * |G_group| stores flag[group] = epoch with release semantics.
+//     wave waits for its stores to complete, the workgroup meets at a
+//     barrier, and one lane releases the tile to device scope and increments
+//     cnt[group]; the lane that brings it to epoch * |G_group| stores
+//     flag[group] = epoch with release semantics.
 #include "../fo_internal.h"
 
 namespace fo {
@@ -51,6 +52,7 @@ constexpr int kThreads = 256;
 constexpr int BK = 64;
 constexpr int kRowBytes = BK * 2;               // one staged row of A or B
 constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw buffer, 32-bit data format
+constexpr int kVmcntZero = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 
 template <typename T>
 __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c);
@@ -224,9 +226,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
 
     // ---- signal: counting table, then the group's flag
     if (p.cnt) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's tile stores, device-wide
+      // Each wave waits until its own tile stores are complete; after the
+      // barrier one lane releases the whole workgroup's stores to device scope
+      // (a single L2 write-back per tile) before it counts the tile.
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
       __syncthreads();
       if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(&p.cnt[t.group], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool fire = old + 1u == p.epoch * (uint32_t)p.thr[t.group];
         if (fire) __hip_atomic_store(&p.flag[t.group], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);

@@ -6,9 +6,10 @@ through the signal words (counting table + flags); the host orders only
 consecutive passes (the next GEMM reuses the reordered buffer, so stream A
 waits for the previous pass's reorder to finish).
 
-Launch order: the GEMM is enqueued before the consumer.  The GEMM never
-waits for anything, so even if both streams ended up on one hardware queue
-the pass would complete (serialised, without overlap).
+Streams: both come from ``fo_stream_create``, so each has a hardware queue of
+its own and the consumer really runs beside the GEMM.  Launch order: the GEMM
+is enqueued before the consumer; the GEMM never waits for anything, so even
+streams that shared a queue would complete (serialised, without overlap).
 
 Buffers (torch tensors, 16-bit elements stored as int16):
   A [M*K], B [problems*N*K], reorder_buf / peer / recv / out [M*N],
@@ -19,7 +20,7 @@ from __future__ import annotations
 
 from typing import Optional
 
-from . import Plan
+from . import Plan, stream_create, stream_destroy
 
 
 class Pipeline:
@@ -36,8 +37,10 @@ class Pipeline:
         self.out = torch.empty(n, dtype=torch.int16, device=dev)
         self.sig = torch.zeros(max(1, 2 * plan.P), dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.sa = torch.cuda.Stream(device=dev)
-        self.sb = torch.cuda.Stream(device=dev)
+        # each side gets a hardware queue of its own, or the consumer would run after the GEMM
+        with torch.cuda.device(dev):
+            self.sa = stream_create()
+            self.sb = stream_create()
         self.done_b = torch.cuda.Event()
         self.epoch = 0
         self.consumer_workgroups = consumer_workgroups
@@ -49,7 +52,22 @@ class Pipeline:
         self.sb.wait_event(ready)
         self.done_b.record(self.sb)
 
-    def step(self, trace=None, events: Optional[dict] = None):
+    def close(self):
+        """Wait for the streams, then release them."""
+        if getattr(self, "sa", None) is not None:
+            self.sa.synchronize()
+            self.sb.synchronize()
+            stream_destroy(self.sa)
+            stream_destroy(self.sb)
+            self.sa = self.sb = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def step(self, trace=None, consumer_trace=None, events: Optional[dict] = None):
         """Enqueue one pass; returns the epoch it used.  ``events`` may hold
         torch.cuda.Event pairs recorded around each kernel on its own stream:
         keys 'gemm', 'consume', 'post' -> (start, end)."""
@@ -64,7 +82,8 @@ class Pipeline:
             events["gemm"][1].record(self.sa)
             events["consume"][0].record(self.sb)
         p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status,
-                        timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups, stream=self.sb)
+                        timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
+                        trace=consumer_trace, stream=self.sb)
         if events:
             events["consume"][1].record(self.sb)
             events["post"][0].record(self.sb)

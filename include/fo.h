@@ -111,6 +111,7 @@ typedef struct fo_plan_info {
   int32_t num_units;               /* consumer work units (collective calls) over all groups  */
   int32_t mode, ranks, dtype, num_problems;
   int32_t device;                  /* HIP device the tables live on; -1 if host-only          */
+  int32_t clock_khz;               /* rate of the device wall clock used by the traces; 0 if host-only */
 } fo_plan_info;
 
 /*
@@ -192,20 +193,35 @@ int fo_gemm_plain(const fo_plan *plan, const void *A, const void *B, void *C, hi
  *      waits longer stores FO_ERR_TIMEOUT into *dev_status (if it was still
  *      0) and every workgroup then stops; later spans are left untouched.
  * dev_status: device int32, caller zeroes it; read it after synchronising.
- * The GEMM that raises the flags must run on a different stream; the two
- * are linked only through sig.  The consumer occupies few resources so
- * that it can stay resident beside the GEMM.
+ * trace: NULL, or device uint64[P]: workgroup 0 stores the wall clock at the
+ *      moment its wait for group g ended (same clock as fo_gemm_signal's
+ *      trace), so a caller can see the consumer start a group while the
+ *      GEMM is still running.
+ * The GEMM that raises the flags must run on a different stream (see
+ * fo_stream_create); the two are linked only through sig.  The consumer
+ * occupies few resources so that it can stay resident beside the GEMM.
  */
 int fo_consume_group(const fo_plan *plan, const void *send, const void *peer, void *recv,
                      const uint32_t *sig, uint32_t epoch, int32_t g_begin, int32_t g_end,
                      int32_t *dev_status, uint64_t timeout_us, int32_t num_workgroups,
-                     hipStream_t stream);
+                     uint64_t *trace, hipStream_t stream);
 
 /* Post-communication reordering: out[m*N + n] = reordered[off(m, n)] (inverse mapping). */
 int fo_reorder_post(const fo_plan *plan, const void *reordered, void *out, hipStream_t stream);
 
 /* Pre-communication reordering as a separate pass: reordered[off(m, n)] = in[m*N + n]. */
 int fo_reorder_pre(const fo_plan *plan, const void *in, void *reordered, hipStream_t stream);
+
+/*
+ * A stream for the GEMM or the consumer side: a HIP stream on the current
+ * device with a hardware queue of its own (created with a CU mask that
+ * enables every CU, default priority).  Streams that share a hardware queue
+ * run their kernels one after another, which would serialise the consumer
+ * behind the GEMM instead of running it alongside.  Destroy with
+ * fo_stream_destroy.
+ */
+int fo_stream_create(hipStream_t *out);
+int fo_stream_destroy(hipStream_t stream);
 
 /* Static description of a status code. */
 const char *fo_status_string(int code);

@@ -55,3 +55,27 @@ def tol_check(gpu_bits, ref_f64, dtype: str, what: str):
                              f"gpu {g.ravel()[i]!r} oracle {r.ravel()[i]!r}")
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     return float(err.max() / rms) if rms > 0 and err.size else 0.0
+
+
+def tol_check_out(gpu_bits, want_out, c_ref, dtype: str, what: str):
+    """Tolerance for out = round(C + peer), derived from the GEMM's.
+
+    The GEMM output C may differ from the oracle by up to
+    tol_C = 1e-2 * max(1, |C|); the consumer adds peer exactly and rounds
+    once on each side, so |out_gpu - out_oracle| <= tol_C + 2^(1-p) * (|out| + tol_C)
+    with p the significand bits of the type.  Cancellation in C + peer is why
+    the bound follows |C| and not |out|.
+    """
+    p = oracle.DTYPES[dtype]["p"]
+    g = oracle.decode_bits(gpu_bits, dtype)
+    r = np.asarray(want_out, dtype=np.float64)
+    c = np.asarray(c_ref, dtype=np.float64)
+    assert g.shape == r.shape == c.shape, (what, g.shape, r.shape, c.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values in the GPU result"
+    tol_c = 1e-2 * np.maximum(1.0, np.abs(c))
+    bound = tol_c + 2.0 ** (1 - p) * (np.abs(r) + tol_c)
+    bad = np.abs(g - r) > bound
+    if bad.any():
+        i = int(np.argmax(bad.ravel()))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the derived bound; first at {i}: "
+                             f"gpu {g.ravel()[i]!r} oracle {r.ravel()[i]!r} C {c.ravel()[i]!r}")
