@@ -18,12 +18,26 @@
 //     A and B fragments are passed to the MFMA swapped (B as the first
 //     operand) so that every lane ends up with 4 consecutive columns of one
 //     output row, which the epilogue writes as 8-byte pieces.
-//   * BK = 64; A and B tiles are staged through LDS in two buffers: the
-//     global loads of slice k+1 are in flight while slice k is multiplied.
-//     LDS rows are 128 bytes (64 K-elements); 16-byte chunk c of row r is
-//     stored at chunk c ^ (r & 7), so the eight lanes of a ds_read_b128
-//     phase that read the same K-chunk of eight consecutive rows hit eight
-//     different bank groups.
+//   * BK = 64; A and B K-slices go from memory straight into LDS (gfx950
+//     buffer loads with the LDS destination, 16 bytes per lane), through a
+//     ring of three LDS stages: slice k+2 is loaded while slice k is
+//     multiplied, its DMA instructions spread over the multiplication so the
+//     wave never waits on a full memory queue with the matrix pipe idle; no
+//     VGPRs or ds_write instructions are spent on staging.
+//   * LDS rows are 128 bytes (64 K-elements); 16-byte chunk c of row r is
+//     stored at chunk c ^ ((r / 2) % 8).  gfx950's LDS serves 16 lanes of a
+//     ds_read_b128 per cycle over 64 banks (256 bytes): the 16 lanes read the
+//     same K-chunk of 16 consecutive rows, which this swizzle spreads over all
+//     64 banks (rows r and r+1 start in different halves of the banks, and
+//     the XOR term separates the 8 row pairs).  A DMA load writes lane l's 16
+//     bytes at position l of the wave's 1 KiB destination, so each lane
+//     fetches the global chunk that belongs at its position.
+//   * The MFMA accumulators live in the accumulation registers (AGPRs); the
+//     LDS reads of k-step s+1 are issued between the MFMAs of k-step s.
+//   * Each wave waits for its own loads of slice k, then the workgroup meets
+//     at a bare barrier (no memory-model fence, which would drain every
+//     outstanding load); compiler-only fences keep LDS accesses on their side
+//     of it.
 //   * Global loads are buffer loads against a per-tile resource whose size
 //     ends at the tile's last valid row, so rows past an edge read zeros and
 //     never touch memory outside the problem.
@@ -53,6 +67,20 @@ constexpr int BK = 64;
 constexpr int kRowBytes = BK * 2;               // one staged row of A or B
 constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw buffer, 32-bit data format
 constexpr int kVmcntZero = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
+constexpr int kLgkmcntZero = 0xC07F;            // s_waitcnt lgkmcnt(0), other counters unconstrained
+constexpr int kStages = 3;                      // LDS ring depth of the main loop
+
+// s_waitcnt immediate for vmcnt(n) with the other counters unconstrained (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier that does not wait for outstanding memory operations.
+__device__ __forceinline__ void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 template <typename T>
 __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c);
@@ -100,38 +128,47 @@ struct Cfg {
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_PER_T = BM * 8 / kThreads;  // 16-byte chunks per thread per stage
   static constexpr int B_PER_T = BN * 8 / kThreads;
+  static constexpr int LOADS = A_PER_T + B_PER_T;     // DMA instructions per thread per stage
   static constexpr int STAGE = (BM + BN) * kRowBytes;
   static constexpr int OUT_PITCH = BN * 2 + 16;      // bytes per staged output row
   static constexpr int OUT_BYTES = BM * OUT_PITCH;
   static constexpr int ROWOFF = OUT_BYTES;           // int64 per row after the staging tile
-  static constexpr int LDS = (2 * STAGE > OUT_BYTES + BM * 8) ? 2 * STAGE : OUT_BYTES + BM * 8;
+  static constexpr int LDS = (kStages * STAGE > OUT_BYTES + BM * 8) ? kStages * STAGE : OUT_BYTES + BM * 8;
   static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "chunk split");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
+  static_assert(LOADS % 4 == 0, "a slice's DMA instructions split over four blocks");
 };
 
 template <typename T, int BM, int BN>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  // Naming an accumulation register here lets the compiler give the MFMAs
+  // their accumulation-register form, so the accumulators live outside the
+  // 256 architectural VGPRs that the operands, offsets and addresses need.
+#if defined(__HIP_DEVICE_COMPILE__)  // the register name exists only for the GPU target
+  asm volatile("; accumulators in AGPRs" ::: "a0");
+#endif
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations go to M0
   const int wm = wave >> 1, wn = wave & 1;
   const int g = blockIdx.x;
   const int pos = p.remap ? (g & 7) * (p.W >> 3) + (g >> 3) : g;
   const int nk = p.K / BK;
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
 
-  // global -> LDS copy coordinates.  Chunk i of a thread is row tid/8 + 32 i,
-  // 16-byte column tid % 8; the row's swizzle term (row & 7) does not depend
-  // on i, so one base offset per operand plus compile-time strides suffices.
-  const uint32_t g_base = (uint32_t)(tid >> 3) * row_bytes + (uint32_t)(tid & 7) * 16u;
+  // global -> LDS coordinates.  DMA instruction i of wave w fills 1 KiB of
+  // LDS: rows (4 i + w) * 8 .. + 8 of the operand.  Lane l lands at physical
+  // chunk l % 8 of row r = (4 i + w) * 8 + l / 8, which holds the logical
+  // chunk (l % 8) ^ ((r / 2) % 8) = (l % 8) ^ (4 (w % 2) + l / 16); row and
+  // chunk depend on i only through a stride.
+  const uint32_t g_base = (uint32_t)(wave * 8 + (lane >> 3)) * row_bytes +
+                          (uint32_t)(((lane & 7) ^ (4 * (wave & 1) + (lane >> 4))) << 4);
   const uint32_t g_step = 32u * row_bytes;
-  const uint32_t s_base = (uint32_t)((tid >> 3) * kRowBytes + (((tid & 7) ^ ((tid >> 3) & 7)) << 4));
-  constexpr uint32_t s_step = 32u * kRowBytes;
   constexpr uint32_t s_bofs = BM * kRowBytes;      // B rows follow A rows in a stage
   // MFMA fragment reads: row (lane % 32) of each 32-row block, K-chunk ks*2 + lane/32
-  const int frag_row = lane & 31, frag_half = lane >> 5, swz = lane & 7;
+  const int frag_row = lane & 31, frag_half = lane >> 5, swz = (lane >> 1) & 7;
   const uint32_t a_frag = (uint32_t)((wm * C::WM + frag_row) * kRowBytes);
   const uint32_t b_frag = (uint32_t)(s_bofs + (wn * C::WN + frag_row) * kRowBytes);
 
@@ -145,60 +182,128 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
         (void *)(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K), (short)0,
         (int)(t.cols * row_bytes), kRsrcWord3);
 
+    // K-slice kt -> LDS stage kt % 3, as C::LOADS DMA instructions per thread;
+    // part p of 4 issues instructions [p * DPB, (p + 1) * DPB)
+    constexpr int DPB = C::LOADS / 4;
+    auto issue_part = [&](int kt, int part) {
+      char *st = smem + (kt % kStages) * C::STAGE + wave * 1024;
+      const uint32_t soff = (uint32_t)kt * kRowBytes;
+      const int q0 = part * DPB, q1 = q0 + DPB;  // this part's instructions: A rows first, then B rows
+#pragma unroll
+      for (int q = 0; q < C::A_PER_T; ++q)
+        if (q >= q0 && q < q1)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + q * 4096), 16, g_base + q * g_step, soff, 0,
+                                                   0);
+#pragma unroll
+      for (int q = 0; q < C::B_PER_T; ++q)
+        if (C::A_PER_T + q >= q0 && C::A_PER_T + q < q1)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + s_bofs + q * 4096), 16, g_base + q * g_step,
+                                                   soff, 0, 0);
+    };
+    auto issue = [&](int kt) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) issue_part(kt, part);
+    };
+
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
 
-    u32x4 va[C::A_PER_T], vb[C::B_PER_T];
+    // Fragments of one 16-deep k-step of a stage, into register set u, read
+    // in the order the MFMAs below consume them.
+    u32x4 fa[2][C::FM], fb[2][C::FN];
+    auto read_frags = [&](int u, int stage, int ks) {
+      const char *base = smem + (stage % kStages) * C::STAGE;
+      const uint32_t chunk = (uint32_t)(((ks * 2 + frag_half) ^ swz) << 4);
+      fa[u][0] = *reinterpret_cast<const u32x4 *>(base + a_frag + chunk);
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) va[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, g_base + i * g_step, 0, 0);
+      for (int f = 0; f < C::FN; ++f)
+        fb[u][f] = *reinterpret_cast<const u32x4 *>(base + b_frag + f * 32 * kRowBytes + chunk);
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, g_base + i * g_step, 0, 0);
+      for (int f = 1; f < C::FM; ++f)
+        fa[u][f] = *reinterpret_cast<const u32x4 *>(base + a_frag + f * 32 * kRowBytes + chunk);
+    };
+    auto mfmas = [&](int u) {
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) *reinterpret_cast<u32x4 *>(smem + s_base + i * s_step) = va[i];
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) *reinterpret_cast<u32x4 *>(smem + s_bofs + s_base + i * s_step) = vb[i];
-    __syncthreads();
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mma<T>(fb[u][j], fa[u][i], acc[i][j]);
+    };
+    // Order inside a block: its share of DMA loads spread out, its LDS reads
+    // alternating with its MFMAs, so the wave never sits on a queue while the
+    // matrix pipe has nothing to do.
+    constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
+    // (every caller passes a literal, so the branches fold away after inlining)
+    auto block_order = [&](bool dma) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (dma && r % 2 == 0 && r / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        // DS read
+        if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+      }
+      if (dma && (NR + 1) / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, DPB - (NR + 1) / 2, 0);
+      if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = (kt & 1) * C::STAGE;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int soff = (kt + 1) * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < C::A_PER_T; ++i)
-          va[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, g_base + i * g_step, soff, 0);
-#pragma unroll
-        for (int i = 0; i < C::B_PER_T; ++i)
-          vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, g_base + i * g_step, soff, 0);
-      }
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const uint32_t chunk = (uint32_t)(((ks * 2 + frag_half) ^ swz) << 4);
-        u32x4 af[C::FM], bfr[C::FN];
-#pragma unroll
-        for (int f = 0; f < C::FM; ++f)
-          af[f] = *reinterpret_cast<const u32x4 *>(smem + cur + a_frag + f * 32 * kRowBytes + chunk);
-#pragma unroll
-        for (int f = 0; f < C::FN; ++f)
-          bfr[f] = *reinterpret_cast<const u32x4 *>(smem + cur + b_frag + f * 32 * kRowBytes + chunk);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) acc[i][j] = mma<T>(bfr[j], af[i], acc[i][j]);
-      }
-      if (more) {
-        const int nxt = ((kt + 1) & 1) * C::STAGE;
-#pragma unroll
-        for (int i = 0; i < C::A_PER_T; ++i) *reinterpret_cast<u32x4 *>(smem + nxt + s_base + i * s_step) = va[i];
-#pragma unroll
-        for (int i = 0; i < C::B_PER_T; ++i)
-          *reinterpret_cast<u32x4 *>(smem + nxt + s_bofs + s_base + i * s_step) = vb[i];
-      }
-      __syncthreads();
+    // Stage s holds slice s from when it is loaded (during slice s-2) until
+    // its last fragments are read (third k-step of slice s): three LDS stages.
+    // Slice kt+2's loads are spread over the four blocks of slice kt.
+    issue(0);
+    if (nk > 1) {
+      issue(1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
     }
+    bare_barrier();
+    read_frags(0, 0, 0);
+    // The last slice is peeled off so that the loop body has no join point at
+    // which the wait-count insertion would have to assume the worst of two paths.
+    auto three_blocks = [&](int kt, bool dma) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (dma) issue_part(kt + 2, 0);
+      read_frags(1, kt, 1);
+      mfmas(0);
+      block_order(dma);
+      if (dma) issue_part(kt + 2, 1);
+      read_frags(0, kt, 2);
+      mfmas(1);
+      block_order(dma);
+      if (dma) issue_part(kt + 2, 2);
+      read_frags(1, kt, 3);
+      mfmas(0);
+      block_order(dma);
+    };
+    // Steady state: one path per iteration, so the accumulators keep their
+    // registers from one iteration to the next.
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) {
+      three_blocks(kt, true);
+      issue_part(kt + 2, 3);
+      // this wave's reads of slice kt are complete and its loads of slice kt+1 landed
+      __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
+      bare_barrier();  // no wave reads slice kt any more; slice kt+1 is in LDS for every wave
+      read_frags(0, kt + 1, 0);
+      mfmas(1);
+      block_order(false);
+    }
+    if (kt + 1 < nk) {  // the last handover: nothing left to load
+      three_blocks(kt, false);
+      __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      bare_barrier();
+      read_frags(0, kt + 1, 0);
+      mfmas(1);
+      block_order(false);
+    }
+    three_blocks(nk - 1, false);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // all fragment reads done before the staging tile overwrites the ring
 
     // ---- epilogue: destination of every valid row, then the 16-bit tile through LDS
     if (tid < BM) rowoff[tid] = tid < t.rows ? row_offset(p.L, t, b, tid) : 0;
@@ -224,7 +329,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
       }
     }
 
-    // ---- signal: counting table, then the group's flag
+    // ---- signal: counting table, then the group's flag.  Either way the
+    // tile's stores complete here, so the next tile's load counting starts clean.
+    if (!p.cnt) __builtin_amdgcn_s_waitcnt(kVmcntZero);
     if (p.cnt) {
       // Each wave waits until its own tile stores are complete; after the
       // barrier one lane releases the whole workgroup's stores to device scope
