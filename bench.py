@@ -41,6 +41,10 @@ def _args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="profiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc passes: the calibration copy and each kernel launched alone on one "
+                         "stream (counter collection serialises dispatches, which the two-stream pipeline "
+                         "cannot run under)")
     return ap.parse_args()
 
 
@@ -64,6 +68,30 @@ def _time_kernel(torch, launch, stream, n, scratch=None):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the GEMM kernel's sources: ties committed traffic counters to the code they measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("gemm_tile_signaling_amd/csrc/kernels/gemm.hip", "gemm_tile_signaling_amd/csrc/fo_internal.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the signaling GEMM from the committed rocprofv3 counter passes, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"signal_gemm_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, min_seconds=10.0):
@@ -117,6 +145,35 @@ def main():
     flops = 2.0 * w.M * w.N * w.K
     comps = list(w.compositions) or [None]
     scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.int32, device=dev)
+    # a plain copy of known size (256 MiB read, 256 MiB written): the reference that
+    # scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters of the other kernels
+    cal_src = torch.ones(256 * 2 ** 20 // 4, dtype=torch.int32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    if a.counters:
+        plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W,
+                       composition=comps[0], mode=w.mode, ranks=w.ranks, row_dest=row_dest)
+        buf = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
+        out = torch.empty_like(buf)
+        sig = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
+        ready = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
+        ready[plan.P:] = 1
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        for e in range(1, a.steps + 1):
+            plan.gemm_signal(dA, dB, buf, sig, e)
+        for _ in range(a.steps):
+            plan.gemm_plain(dA, dB, out)
+        for _ in range(a.steps):
+            plan.consume_group(buf, dpeer, out, ready, 1, status)
+        for _ in range(a.steps):
+            plan.reorder_post(buf, out)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_pass": w.name, "launches_per_kernel": a.steps,
+                          "calibration_copy_bytes": 256 * 2 ** 20, "status": int(status.item())}), flush=True)
+        return
 
     results = []
     for comp in comps:
@@ -195,7 +252,9 @@ def main():
                    "M": w.M, "N": w.N, "K": w.K, "tile": [w.BM, w.BN], "swizzle": w.S, "wave": w.W,
                    "tiles": plan.NT, "waves": plan.T, "groups": list(best["comp"]), "parallelism": "1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(w.name),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes": 2 * (w.M * w.K + w.N * w.K + w.M * w.N),
                      "kernel": "signaling GEMM (stream A, consumer resident)"},
         "signal_gemm_alone_tflops": round(flops / (signal_ms * 1e-3) / 1e12, 2),
         "plain_gemm_alone_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),

@@ -139,7 +139,10 @@ struct Cfg {
   static_assert(LOADS % 4 == 0, "a slice's DMA instructions split over four blocks");
 };
 
-template <typename T, int BM, int BN>
+// SIGNAL: the signaling GEMM (reordered stores, counting table, flags); otherwise
+// the plain GEMM with a row-major epilogue.  Separate instantiations keep the
+// plain kernel free of signaling code and give the two distinct symbols.
+template <typename T, int BM, int BN, bool SIGNAL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -331,8 +334,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
     // ---- signal: counting table, then the group's flag.  Either way the
     // tile's stores complete here, so the next tile's load counting starts clean.
-    if (!p.cnt) __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    if (p.cnt) {
+    if constexpr (!SIGNAL) __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    if constexpr (SIGNAL) {
       // Each wave waits until its own tile stores are complete; after the
       // barrier one lane releases the whole workgroup's stores to device scope
       // (a single L2 write-back per tile) before it counts the tile.
@@ -355,25 +358,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   }
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, bool SIGNAL>
 int launch_typed(const GemmParams &gp, hipStream_t s) {
   using C = Cfg<BM, BN>;
   static bool configured = false;  // per process; the attribute is per kernel and device-independent
   if (!configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, SIGNAL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
       return FO_ERR_HIP;
     configured = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN>), dim3(gp.W), dim3(kThreads), C::LDS, s, gp);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, SIGNAL>), dim3(gp.W), dim3(kThreads), C::LDS, s, gp);
   return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
 }
 
-template <typename T>
+template <typename T, bool SIGNAL>
 int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
-  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128>(gp, s);
-  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128>(gp, s);
-  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64>(gp, s);
+  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, SIGNAL>(gp, s);
+  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, SIGNAL>(gp, s);
+  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, SIGNAL>(gp, s);
   return FO_ERR_UNSUPPORTED;
 }
 
@@ -400,7 +403,9 @@ int launch_gemm(const fo_plan *p, const void *A, const void *B, void *Cout, bool
   gp.trace = sig ? trace : nullptr;
   gp.epoch = epoch;
   gp.P = p->P;
-  return p->dtype == FO_BF16 ? launch_tile<__bf16>(p, gp, s) : launch_tile<_Float16>(p, gp, s);
+  const bool sig_on = gp.cnt != nullptr;
+  if (p->dtype == FO_BF16) return sig_on ? launch_tile<__bf16, true>(p, gp, s) : launch_tile<__bf16, false>(p, gp, s);
+  return sig_on ? launch_tile<_Float16, true>(p, gp, s) : launch_tile<_Float16, false>(p, gp, s);
 }
 
 }  // namespace fo

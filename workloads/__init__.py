@@ -37,7 +37,7 @@ class Workload:
     seed_base: int               # seeds seed_base + 1 (A), + 2 (B), + 3 (peer), + 4 (routing)
     BM: int = 256
     BN: int = 128
-    S: int = 8                   # swizzle width
+    S: int = 4                   # swizzle width
     W: int = 256                 # wave size (tiles resident at once)
     compositions: Tuple = ()     # wave-group partitions to run; () = all
     mode: str = "tile"
