@@ -11,11 +11,18 @@
 // Design: a persistent grid.  Every workgroup walks the groups in firing
 // order; for each group one lane polls flag[g] (agent-scope loads, s_sleep
 // back-off, bounded by the device wall clock), the workgroup meets at a
-// barrier and acquires device scope, and then all workgroups stream the
-// group's units with 16-byte loads: recv = round(float(send) + float(peer)).
-// The kernel holds no LDS beyond one word and few registers, so it can stay
-// resident next to the GEMM's workgroups.
+// barrier, and then all workgroups stream the group's units with 16-byte
+// buffer loads: recv = round(float(send) + float(peer)).  The span is read
+// with device-coherent loads (the cache policy that agent-scope atomic loads
+// use), so data the producer released to device scope is read from the point
+// of coherence and no workgroup has to invalidate its L2 (a full-L2
+// invalidation per workgroup per group would evict the GEMM's operands and,
+// with many workgroups, dominate the kernel).  Each unit gets its own buffer
+// resources, so the tail needs no branches: loads past the end read zeros and
+// stores past the end are dropped.  The kernel holds no LDS beyond one word
+// and few registers, so it can stay resident next to the GEMM's workgroups.
 #include "../fo_internal.h"
+#include "buffer.h"
 
 namespace fo {
 namespace {
@@ -26,7 +33,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;          // 16-byte chunks in flight per thread
+constexpr int kCoherent = 16;       // buffer cache policy: device-coherent load
 
 struct ConsumeParams {
   const uint16_t *send;
@@ -64,7 +72,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
   __shared__ int s_go;
   const int tid = threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const uint32_t stride = gridDim.x * kThreads;
   for (int g = p.g_begin; g < p.g_end; ++g) {
     if (tid == 0) {
       int go = 1;
@@ -93,25 +101,26 @@ __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
     const int go = s_go;
     __syncthreads();  // s_go is rewritten for the next group
     if (!go) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the producer's tile stores become visible
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no span load is hoisted above the wait
 
     for (int u = p.group_unit[g]; u < p.group_unit[g + 1]; ++u) {
-      const int64_t lo = p.unit_off[u] >> 3, hi = p.unit_off[u + 1] >> 3;  // 16-byte chunks
-      for (int64_t c0 = lo + (int64_t)blockIdx.x * kThreads + tid; c0 < hi; c0 += kUnroll * stride) {
+      const int64_t lo = p.unit_off[u], hi = p.unit_off[u + 1];  // elements, multiples of 8
+      const uint32_t bytes = (uint32_t)((hi - lo) * 2);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.send + lo, bytes);
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.peer + lo, bytes);
+      const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.recv + lo, bytes);
+      const uint32_t n = bytes >> 4;  // 16-byte chunks in the unit
+      for (uint32_t c0 = blockIdx.x * kThreads + tid; c0 < n; c0 += kUnroll * stride) {
         u32x4 a[kUnroll], b[kUnroll];
 #pragma unroll
         for (int i = 0; i < kUnroll; ++i) {
-          const int64_t c = c0 + i * stride;
-          if (c < hi) {
-            a[i] = *reinterpret_cast<const u32x4 *>(p.send + c * 8);
-            b[i] = *reinterpret_cast<const u32x4 *>(p.peer + c * 8);
-          }
+          const uint32_t off = (c0 + i * stride) * 16u;
+          a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent);
+          b[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < kUnroll; ++i) {
-          const int64_t c = c0 + i * stride;
-          if (c < hi) *reinterpret_cast<u32x4 *>(p.recv + c * 8) = add8<T>(a[i], b[i]);
-        }
+        for (int i = 0; i < kUnroll; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(add8<T>(a[i], b[i]), rr, (c0 + i * stride) * 16u, 0, 0);
       }
     }
   }

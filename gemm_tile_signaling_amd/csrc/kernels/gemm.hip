@@ -49,6 +49,7 @@
 //     cnt[group]; the lane that brings it to epoch * |G_group| stores
 //     flag[group] = epoch with release semantics.
 #include "../fo_internal.h"
+#include "buffer.h"
 
 namespace fo {
 namespace {
@@ -65,7 +66,6 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 constexpr int kThreads = 256;
 constexpr int BK = 64;
 constexpr int kRowBytes = BK * 2;               // one staged row of A or B
-constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw buffer, 32-bit data format
 constexpr int kVmcntZero = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 constexpr int kLgkmcntZero = 0xC07F;            // s_waitcnt lgkmcnt(0), other counters unconstrained
 constexpr int kStages = 3;                      // LDS ring depth of the main loop
@@ -93,6 +93,22 @@ template <>
 __device__ __forceinline__ f32x16 mma<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                 0, 0);
+}
+
+// Part PART of a K-slice's LDS-DMA loads: DPB consecutive instructions of the
+// thread's A_PER_T (A rows) then B_PER_T (B rows).  Lane l of instruction q
+// lands at LDS offset dst + q' * 4096 + 16 l of its operand's region.
+template <int PART, int DPB, int A_PER_T, int B_PER_T>
+__device__ __forceinline__ void dma_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, char *dst,
+                                         uint32_t b_region, uint32_t g_base, uint32_t g_step, uint32_t soff) {
+  constexpr int q0 = PART * DPB, q1 = q0 + DPB;
+#pragma unroll
+  for (int q = q0; q < (q1 < A_PER_T ? q1 : A_PER_T); ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(dst + q * 4096), 16, g_base + q * g_step, soff, 0, 0);
+#pragma unroll
+  for (int q = (q0 > A_PER_T ? q0 : A_PER_T); q < q1; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(dst + b_region + (q - A_PER_T) * 4096), 16,
+                                             g_base + (q - A_PER_T) * g_step, soff, 0, 0);
 }
 
 template <typename T>
@@ -179,33 +195,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
   for (int b = pos; b < p.NT; b += p.W) {
     const TileDesc t = p.slots[b];
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.A + (int64_t)t.row0 * p.K), (short)0, (int)(t.rows * row_bytes), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K), (short)0,
-        (int)(t.cols * row_bytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)t.row0 * p.K, t.rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K,
+                                                t.cols * row_bytes);
 
     // K-slice kt -> LDS stage kt % 3, as C::LOADS DMA instructions per thread;
     // part p of 4 issues instructions [p * DPB, (p + 1) * DPB)
     constexpr int DPB = C::LOADS / 4;
-    auto issue_part = [&](int kt, int part) {
-      char *st = smem + (kt % kStages) * C::STAGE + wave * 1024;
-      const uint32_t soff = (uint32_t)kt * kRowBytes;
-      const int q0 = part * DPB, q1 = q0 + DPB;  // this part's instructions: A rows first, then B rows
-#pragma unroll
-      for (int q = 0; q < C::A_PER_T; ++q)
-        if (q >= q0 && q < q1)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + q * 4096), 16, g_base + q * g_step, soff, 0,
-                                                   0);
-#pragma unroll
-      for (int q = 0; q < C::B_PER_T; ++q)
-        if (C::A_PER_T + q >= q0 && C::A_PER_T + q < q1)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + s_bofs + q * 4096), 16, g_base + q * g_step,
-                                                   soff, 0, 0);
-    };
+    // parts of slice kt's loads (stage kt % 3)
+    auto stage_dst = [&](int kt) { return smem + (kt % kStages) * C::STAGE + wave * 1024; };
+#define FO_DMA_PART(PART, KT)                                                                              \
+  dma_part<PART, DPB, C::A_PER_T, C::B_PER_T>(ra, rb, stage_dst(KT), s_bofs, g_base, g_step,              \
+                                              (uint32_t)(KT) * kRowBytes)
     auto issue = [&](int kt) {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) issue_part(kt, part);
+      FO_DMA_PART(0, kt);
+      FO_DMA_PART(1, kt);
+      FO_DMA_PART(2, kt);
+      FO_DMA_PART(3, kt);
     };
 
     f32x16 acc[C::FM][C::FN];
@@ -238,15 +244,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // alternating with its MFMAs, so the wave never sits on a queue while the
     // matrix pipe has nothing to do.
     constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
-    // (every caller passes a literal, so the branches fold away after inlining)
-    auto block_order = [&](bool dma) {
+    auto block_order_dma = [&]() {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        if (dma && r % 2 == 0 && r / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        // DS read
-        if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // MFMA
+        if (r % 2 == 0 && r / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                 // DS read
+        if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
       }
-      if (dma && (NR + 1) / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, DPB - (NR + 1) / 2, 0);
+      if ((NR + 1) / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, DPB - (NR + 1) / 2, 0);
+      if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto block_order = [&]() {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
       if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -265,47 +279,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     read_frags(0, 0, 0);
     // The last slice is peeled off so that the loop body has no join point at
     // which the wait-count insertion would have to assume the worst of two paths.
-    auto three_blocks = [&](int kt, bool dma) {
+    auto three_blocks_dma = [&](int kt) {  // and three quarters of slice kt+2's loads
       __builtin_amdgcn_sched_barrier(0);
-      if (dma) issue_part(kt + 2, 0);
+      FO_DMA_PART(0, kt + 2);
       read_frags(1, kt, 1);
       mfmas(0);
-      block_order(dma);
-      if (dma) issue_part(kt + 2, 1);
+      block_order_dma();
+      FO_DMA_PART(1, kt + 2);
       read_frags(0, kt, 2);
       mfmas(1);
-      block_order(dma);
-      if (dma) issue_part(kt + 2, 2);
+      block_order_dma();
+      FO_DMA_PART(2, kt + 2);
       read_frags(1, kt, 3);
       mfmas(0);
-      block_order(dma);
+      block_order_dma();
+    };
+    auto three_blocks = [&](int kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(1, kt, 1);
+      mfmas(0);
+      block_order();
+      read_frags(0, kt, 2);
+      mfmas(1);
+      block_order();
+      read_frags(1, kt, 3);
+      mfmas(0);
+      block_order();
     };
     // Steady state: one path per iteration, so the accumulators keep their
     // registers from one iteration to the next.
     int kt = 0;
     for (; kt + 2 < nk; ++kt) {
-      three_blocks(kt, true);
-      issue_part(kt + 2, 3);
+      three_blocks_dma(kt);
+      FO_DMA_PART(3, kt + 2);
       // this wave's reads of slice kt are complete and its loads of slice kt+1 landed
       __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
       bare_barrier();  // no wave reads slice kt any more; slice kt+1 is in LDS for every wave
       read_frags(0, kt + 1, 0);
       mfmas(1);
-      block_order(false);
+      block_order();
     }
     if (kt + 1 < nk) {  // the last handover: nothing left to load
-      three_blocks(kt, false);
+      three_blocks(kt);
       __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
       bare_barrier();
       read_frags(0, kt + 1, 0);
       mfmas(1);
-      block_order(false);
+      block_order();
     }
-    three_blocks(nk - 1, false);
+    three_blocks(nk - 1);
     mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
+#undef FO_DMA_PART
     __syncthreads();  // all fragment reads done before the staging tile overwrites the ring
 
     // ---- epilogue: destination of every valid row, then the 16-bit tile through LDS

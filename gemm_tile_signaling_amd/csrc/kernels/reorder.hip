@@ -9,16 +9,21 @@
 //
 // Design: pure data movement, bound by HBM bandwidth.  One workgroup per
 // (slot, band of up to 128 tile rows); every row of a tile is a contiguous
-// run of `cols` elements on both sides, so all accesses are 16-byte vector
-// loads and stores.  The destination/source offset of each row is computed
-// once into LDS, then each thread issues all of its loads before its stores.
+// run of `cols` elements on both sides, so all accesses are 16-byte buffer
+// loads and stores with 32-bit offsets (the plan keeps M*N below 2^31).  The
+// source and destination offset of each row are computed once into LDS;
+// chunks outside the tile get an offset past the buffer's end, which the
+// buffer bounds check turns into a zero load and a dropped store, so there
+// are no branches; each thread issues all of its loads before its stores.
 #include "../fo_internal.h"
+#include "buffer.h"
 
 namespace fo {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kThreads = 256;
+constexpr uint32_t kOutside = 0xFFFFFFF0u;  // byte offset past every buffer: zero load, dropped store
 
 struct ReorderParams {
   const uint16_t *src;
@@ -26,39 +31,39 @@ struct ReorderParams {
   const TileDesc *slots;
   Layout L;
   int64_t N;
+  uint32_t bytes;  // 2 * M * N, the size of both buffers
   int32_t to_rowmajor;
 };
 
 template <int RPB, int CPR>  // rows per block, 16-byte chunks per tile row
 __global__ __launch_bounds__(kThreads) void reorder_kernel(ReorderParams p) {
-  __shared__ int64_t ro[RPB];
+  __shared__ uint32_t src_row[RPB], dst_row[RPB];  // byte offsets of each row's first element
   constexpr int kPer = RPB * CPR / kThreads;
   static_assert(RPB * CPR % kThreads == 0, "split");
   const int slot = blockIdx.x;
   const int r0 = blockIdx.y * RPB;
   const TileDesc t = p.slots[slot];
   const int tid = threadIdx.x;
-  if (tid < RPB && r0 + tid < t.rows) ro[tid] = row_offset(p.L, t, slot, r0 + tid);
+  if (tid < RPB && r0 + tid < t.rows) {
+    const uint32_t reo = (uint32_t)row_offset(p.L, t, slot, r0 + tid) * 2u;
+    const uint32_t rm = (uint32_t)((int64_t)(t.row0 + r0 + tid) * p.N + t.col0) * 2u;
+    src_row[tid] = p.to_rowmajor ? reo : rm;
+    dst_row[tid] = p.to_rowmajor ? rm : reo;
+  }
   __syncthreads();
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.src, p.bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dst, p.bytes);
   u32x4 v[kPer];
+  uint32_t dst_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = tid + i * kThreads, r = q / CPR, c8 = q % CPR;
-    if (r0 + r < t.rows && c8 * 8 < t.cols) {
-      const int64_t rm = (int64_t)(t.row0 + r0 + r) * p.N + t.col0 + c8 * 8;
-      const int64_t src = p.to_rowmajor ? ro[r] + c8 * 8 : rm;
-      v[i] = *reinterpret_cast<const u32x4 *>(p.src + src);
-    }
+    const bool in = r0 + r < t.rows && c8 * 8 < t.cols;
+    v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? src_row[r] + c8 * 16u : kOutside, 0, 0);
+    dst_off[i] = in ? dst_row[r] + c8 * 16u : kOutside;
   }
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int q = tid + i * kThreads, r = q / CPR, c8 = q % CPR;
-    if (r0 + r < t.rows && c8 * 8 < t.cols) {
-      const int64_t rm = (int64_t)(t.row0 + r0 + r) * p.N + t.col0 + c8 * 8;
-      const int64_t dst = p.to_rowmajor ? rm : ro[r] + c8 * 8;
-      *reinterpret_cast<u32x4 *>(p.dst + dst) = v[i];
-    }
-  }
+  for (int i = 0; i < kPer; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], rd, dst_off[i], 0, 0);
 }
 
 }  // namespace
@@ -71,6 +76,7 @@ int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajo
   rp.slots = p->d_slots;
   rp.L = p->layout(true);
   rp.N = p->N;
+  rp.bytes = (uint32_t)(2 * p->M * p->N);
   rp.to_rowmajor = to_rowmajor ? 1 : 0;
   if (p->BN == 128) {
     constexpr int RPB = 128;

@@ -104,7 +104,11 @@ int build(const fo_plan_desc *d, fo_plan *p) {
     if (m < 0) return FO_ERR_INVALID;
     M += m;
   }
-  if (M > INT32_MAX || M * p->N > (int64_t(1) << 40)) return FO_ERR_INVALID;
+  if (M > INT32_MAX) return FO_ERR_INVALID;
+  // The consumer and the reorders address each buffer with 32-bit byte offsets:
+  // at most 2^30 elements (2 GiB) keeps every offset they form, including the
+  // ones a thread computes past the end of a unit, below 2^32.
+  if (M * p->N > (int64_t(1) << 30)) return FO_ERR_UNSUPPORTED;
   p->M = M;
 
   if (p->mode == FO_MODE_SUBTILE) {

@@ -86,7 +86,7 @@ typedef enum fo_mode {
 typedef struct fo_plan_desc {
   int32_t num_problems;            /* >= 1                                                    */
   const int64_t *m_per_problem;    /* host [num_problems]: rows of each problem (>= 0)        */
-  int64_t N, K;                    /* N % 8 == 0, K % 64 == 0, both > 0                        */
+  int64_t N, K;                    /* N % 8 == 0, K % 64 == 0, both > 0; M*N <= 2^30          */
   int32_t dtype;                   /* fo_dtype                                                */
   int32_t BM, BN;                  /* tile: 256x128, 128x128 or 64x64; 0,0 = 256x128          */
   int32_t swizzle;                 /* S >= 1; 0 = 4                                           */

@@ -52,6 +52,9 @@ def test_plan_argument_errors():
                            host_only=True)) == -1
     assert _code(lambda: P(128, 128, 64, BM=64, BN=64, dispatch_order=[0, 0, 1, 2], host_only=True)) == -1
     assert _code(lambda: P([-1], 64, 64, host_only=True)) == -1
+    # buffers are addressed with 32-bit byte offsets: M * N may not exceed 2^30 elements
+    assert _code(lambda: P(2 ** 15 + 1, 2 ** 15, 64, host_only=True)) == -2
+    assert P(2 ** 15, 2 ** 15, 64, host_only=True).M == 2 ** 15
 
 
 def test_enqueue_on_host_only_plan_is_rejected():

@@ -12,7 +12,7 @@ import pytest
 import oracle
 from oracle.layout import element_offsets, group_spans
 from oracle.tiles import make_plan
-from tests.gpu_util import empty16, say, to_dev, to_host, tol_check, zeros_i32
+from tests.gpu_util import empty16, say, to_dev, to_host, tol_check, tol_check_out, zeros_i32
 from workloads import draw, random_bits, to_bits
 
 pytestmark = pytest.mark.gpu
@@ -240,3 +240,61 @@ def test_gemm_each_workgroup_runs_its_wave_slot():
     for g in range(4):
         t = ts[g::4]
         assert np.all(np.diff(t) >= 0)
+
+
+# --------------------------------------------------------------------------- addressing
+
+def _views_above_bit31(sizes16):
+    """Views of one allocation, each 256-byte aligned at an address whose low 32-bit word has bit 31 set.
+
+    The kernels build buffer resources from 64-bit addresses split into two
+    32-bit halves; a half widened as a signed value would corrupt the base
+    only for such addresses, which the allocator hands out or not by chance.
+    """
+    total = sum((n * 2 + 255) // 256 * 256 for n in sizes16)
+    assert total < 2 ** 31
+    big = torch.empty(2 ** 32 + total, dtype=torch.uint8, device="cuda")
+    base = big.data_ptr()
+    start = (2 ** 31 - (base & 0xFFFFFFFF)) % 2 ** 32   # next address whose low word is exactly 2^31
+    views, off = [], start
+    for n in sizes16:
+        v = big[off:off + 2 * n].view(torch.int16)
+        assert v.data_ptr() & 0x80000000 and v.data_ptr() % 256 == 0
+        views.append(v)
+        off += (n * 2 + 255) // 256 * 256
+    return big, views
+
+
+def test_every_kernel_with_buffers_above_bit31_of_the_low_word():
+    entry = PLANS[2]                                   # ragged_128: several tiles, ragged edges
+    o, p = _plans(entry)
+    dt = entry[4]
+    MN = o.M * o.N
+    A, B, peer = _inputs(entry, seed=400)
+    Bs = _stack(B)
+    Xh = random_bits(41, MN, dt)
+    r = oracle.run_pipeline(A, B, peer, o, dt)
+    c_send = oracle.pre_reorder(r["C64"], r["off"])
+    say(f"high addresses {entry[0]} M={o.M} N={o.N} K={p.K}")
+    big, (dA, dB, dpeer, C, buf, recv, out, X, Y) = _views_above_bit31([A.size, Bs.size] + [MN] * 7)
+    dA.copy_(to_dev(A).reshape(-1))
+    dB.copy_(to_dev(Bs).reshape(-1))
+    dpeer.copy_(to_dev(peer).reshape(-1))
+    X.copy_(to_dev(Xh).reshape(-1))
+    for v in (C, buf, recv, out, Y):
+        v.fill_(0x7FC0)
+    sig = zeros_i32(2 * p.P)
+    status = zeros_i32(1)
+    p.gemm_plain(dA, dB, C)
+    p.gemm_signal(dA, dB, buf, sig, 1)
+    p.consume_group(buf, dpeer, recv, sig, 1, status)
+    p.reorder_post(recv, out)
+    p.reorder_pre(X, Y)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    tol_check(to_host(C).reshape(o.M, o.N), r["C64"], dt, "C")
+    tol_check(to_host(buf), c_send, dt, "reorder_buf")
+    tol_check_out(to_host(recv), oracle.decode_bits(r["recv"], dt), c_send, dt, "recv")
+    tol_check_out(to_host(out).reshape(o.M, o.N), oracle.decode_bits(r["out"], dt), r["C64"], dt, "out")
+    assert np.array_equal(to_host(Y), oracle.pre_reorder(Xh.reshape(o.M, o.N), r["off"]))
+    del big
