@@ -74,7 +74,8 @@ def kernel_source_hash() -> str:
     """sha256 over the GEMM kernel's sources: ties committed traffic counters to the code they measured."""
     import hashlib
     h = hashlib.sha256()
-    for rel in ("gemm_tile_signaling_amd/csrc/kernels/gemm.hip", "gemm_tile_signaling_amd/csrc/fo_internal.h"):
+    for rel in ("gemm_tile_signaling_amd/csrc/kernels/gemm.hip", "gemm_tile_signaling_amd/csrc/kernels/buffer.h",
+                "gemm_tile_signaling_amd/csrc/fo_internal.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

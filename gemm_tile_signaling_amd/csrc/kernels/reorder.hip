@@ -15,6 +15,7 @@
 // chunks outside the tile get an offset past the buffer's end, which the
 // buffer bounds check turns into a zero load and a dropped store, so there
 // are no branches; each thread issues all of its loads before its stores.
+// Loads and stores are nontemporal: every byte is moved exactly once.
 #include "../fo_internal.h"
 #include "buffer.h"
 
@@ -24,6 +25,7 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kThreads = 256;
 constexpr uint32_t kOutside = 0xFFFFFFF0u;  // byte offset past every buffer: zero load, dropped store
+constexpr int kNT = 2;                       // buffer cache policy: nontemporal (each byte is moved once)
 
 struct ReorderParams {
   const uint16_t *src;
@@ -59,11 +61,11 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(ReorderParams p) {
   for (int i = 0; i < kPer; ++i) {
     const int q = tid + i * kThreads, r = q / CPR, c8 = q % CPR;
     const bool in = r0 + r < t.rows && c8 * 8 < t.cols;
-    v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? src_row[r] + c8 * 16u : kOutside, 0, 0);
+    v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? src_row[r] + c8 * 16u : kOutside, 0, kNT);
     dst_off[i] = in ? dst_row[r] + c8 * 16u : kOutside;
   }
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], rd, dst_off[i], 0, 0);
+  for (int i = 0; i < kPer; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], rd, dst_off[i], 0, kNT);
 }
 
 }  // namespace
