@@ -11,15 +11,19 @@
 // Design: a persistent grid.  Every workgroup walks the groups in firing
 // order; for each group one lane polls flag[g] (agent-scope loads, s_sleep
 // back-off, bounded by the device wall clock), the workgroup meets at a
-// barrier, and then all workgroups stream the group's units with 16-byte
-// buffer loads: recv = round(float(send) + float(peer)).  The span is read
+// barrier, and then all workgroups stream the group's span with 16-byte
+// buffer loads: recv = round(float(send) + float(peer)).  The span is the
+// concatenation of the group's work units (one per collective call in a
+// multi-GPU consumer: the whole span, R rank segments or D destination
+// buckets); the stand-in's reduction is the same on each, so it streams the
+// span in one pass rather than paying a pass per unit.  The span is read
 // with device-coherent loads (the cache policy that agent-scope atomic loads
 // use), so data the producer released to device scope is read from the point
 // of coherence and no workgroup has to invalidate its L2 (a full-L2
 // invalidation per workgroup per group would evict the GEMM's operands and,
 // with many workgroups, dominate the kernel).  Every access is nontemporal:
 // each byte is touched once, and streaming it past the caches roughly doubles
-// the bandwidth a kernel of this shape reaches.  Each unit gets its own buffer
+// the bandwidth a kernel of this shape reaches.  Each span gets its own buffer
 // resources, so the tail needs no branches: loads past the end read zeros and
 // stores past the end are dropped.  The kernel holds no LDS beyond one word
 // and few registers, so it can stay resident next to the GEMM's workgroups.
@@ -106,25 +110,25 @@ __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
     if (!go) return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no span load is hoisted above the wait
 
-    for (int u = p.group_unit[g]; u < p.group_unit[g + 1]; ++u) {
-      const int64_t lo = p.unit_off[u], hi = p.unit_off[u + 1];  // elements, multiples of 8
-      const uint32_t bytes = (uint32_t)((hi - lo) * 2);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.send + lo, bytes);
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.peer + lo, bytes);
-      const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.recv + lo, bytes);
-      const uint32_t n = bytes >> 4;  // 16-byte chunks in the unit
-      for (uint32_t c0 = blockIdx.x * kThreads + tid; c0 < n; c0 += kUnroll * stride) {
-        u32x4 a[kUnroll], b[kUnroll];
+    // The group's units tile its span back to back, and every unit gets the
+    // same elementwise reduction, so the span is streamed as one range.
+    const int64_t lo = p.unit_off[p.group_unit[g]], hi = p.unit_off[p.group_unit[g + 1]];  // multiples of 8
+    const uint32_t bytes = (uint32_t)((hi - lo) * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.send + lo, bytes);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.peer + lo, bytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.recv + lo, bytes);
+    const uint32_t n = bytes >> 4;  // 16-byte chunks in the span
+    for (uint32_t c0 = blockIdx.x * kThreads + tid; c0 < n; c0 += kUnroll * stride) {
+      u32x4 a[kUnroll], b[kUnroll];
 #pragma unroll
-        for (int i = 0; i < kUnroll; ++i) {
-          const uint32_t off = (c0 + i * stride) * 16u;
-          a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent | kNT);
-          b[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kNT);
-        }
-#pragma unroll
-        for (int i = 0; i < kUnroll; ++i)
-          __builtin_amdgcn_raw_buffer_store_b128(add8<T>(a[i], b[i]), rr, (c0 + i * stride) * 16u, 0, kNT);
+      for (int i = 0; i < kUnroll; ++i) {
+        const uint32_t off = (c0 + i * stride) * 16u;
+        a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent | kNT);
+        b[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kNT);
       }
+#pragma unroll
+      for (int i = 0; i < kUnroll; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(add8<T>(a[i], b[i]), rr, (c0 + i * stride) * 16u, 0, kNT);
     }
   }
 }

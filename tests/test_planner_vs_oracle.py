@@ -39,6 +39,11 @@ def _assert_same(o, p):
     flat = [u for g in units for u in g]
     assert uo.tolist() == [u[0] for u in flat] + [flat[-1][1] if flat else 0]
     assert gu.tolist() == [0] + list(np.cumsum([len(g) for g in units]))
+    # each group's units tile its span back to back (the consumer streams the span in one pass)
+    span = t["span_off"].tolist()
+    assert np.all(np.diff(uo) >= 0)
+    for g in range(p.P):
+        assert uo[gu[g]] == span[g] and uo[gu[g + 1]] == span[g + 1]
     assert np.array_equal(p.offsets(), element_offsets(o))
 
 
