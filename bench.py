@@ -159,9 +159,9 @@ def main():
                        composition=comps[0], mode=w.mode, ranks=w.ranks, row_dest=row_dest)
         buf = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
         out = torch.empty_like(buf)
-        sig = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
-        ready = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
-        ready[plan.P:] = 1
+        sig = plan.new_sig(dev)
+        ready = plan.new_sig(dev)
+        plan.flag_of(ready).fill_(1)
         status = torch.zeros(1, dtype=torch.int32, device=dev)
         for e in range(1, a.steps + 1):
             plan.gemm_signal(dA, dB, buf, sig, e)
@@ -220,7 +220,7 @@ def main():
     n_alone = max(10, min(a.steps, 50))
     C = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
     plain_ms = _time_kernel(torch, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, n_alone)
-    sig = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
+    sig = plan.new_sig(dev)
     ep = [0]
 
     def _sig(st):
@@ -228,8 +228,8 @@ def main():
         plan.gemm_signal(dA, dB, pipe.buf, sig, ep[0], stream=st)
     signal_ms = _time_kernel(torch, _sig, s, n_alone)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ready = torch.zeros(2 * plan.P, dtype=torch.int32, device=dev)
-    ready[plan.P:] = 1
+    ready = plan.new_sig(dev)
+    plan.flag_of(ready).fill_(1)
     recv = torch.empty_like(pipe.buf)
     consume_ms = _time_kernel(torch, lambda st: plan.consume_group(pipe.buf, dpeer, recv, ready, 1, status, stream=st),
                               s, n_alone, scratch)

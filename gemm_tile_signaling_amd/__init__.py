@@ -52,7 +52,8 @@ class _Desc(C.Structure):
 class _Info(C.Structure):
     _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64)] + [
         (n, C.c_int32) for n in ("BM", "BN", "swizzle", "wave_size", "NT", "T", "P", "num_units",
-                                 "mode", "ranks", "dtype", "num_problems", "device", "clock_khz")]
+                                 "mode", "ranks", "dtype", "num_problems", "device", "clock_khz",
+                                 "sig_words", "flag_offset")]
 
 
 _lib = None
@@ -179,7 +180,7 @@ class Plan:
         self.info = {n: getattr(info, n) for n, _ in _Info._fields_}
         self.dtype = dtype
         self.mode = mode
-        for k in ("M", "N", "K", "BM", "BN", "NT", "T", "P", "num_units"):
+        for k in ("M", "N", "K", "BM", "BN", "NT", "T", "P", "num_units", "sig_words", "flag_offset"):
             setattr(self, k, self.info[k])
         self.W = self.info["wave_size"]
         self.S = self.info["swizzle"]
@@ -214,12 +215,27 @@ class Plan:
     def mn(self) -> int:
         return self.M * self.N
 
+    def new_sig(self, device="cuda"):
+        """A zeroed signal buffer, int32[sig_words] (at least one word): cnt[P] from word 0 and
+        flag[P] from word flag_offset.  torch's allocations are 256-byte aligned, which keeps the
+        flags on cache lines apart from the counters."""
+        import torch
+        return torch.zeros(max(1, self.sig_words), dtype=torch.int32, device=device)
+
+    def cnt_of(self, sig):
+        """The counting-table words cnt[P] of a signal buffer (a view)."""
+        return sig[:self.P]
+
+    def flag_of(self, sig):
+        """The flag words flag[P] of a signal buffer (a view)."""
+        return sig[self.flag_offset:self.flag_offset + self.P]
+
     def gemm_signal(self, A, B, reorder_buf, sig, epoch: int, trace=None, stream=None):
         _check(lib().fo_gemm_signal(
             self._h, _ptr(A, numel=self.M * self.K, itemsize=2, name="A"),
             _ptr(B, numel=self.num_problems * self.N * self.K, itemsize=2, name="B"),
             _ptr(reorder_buf, numel=self.mn, itemsize=2, name="reorder_buf"),
-            _ptr(sig, numel=2 * self.P, itemsize=4, name="sig"), int(epoch),
+            _ptr(sig, numel=self.sig_words, itemsize=4, name="sig"), int(epoch),
             _ptr(trace, numel=2 * self.NT + self.P, itemsize=8, name="trace"), _stream(stream)), "fo_gemm_signal")
 
     def gemm_plain(self, A, B, Cout, stream=None):
@@ -234,7 +250,7 @@ class Plan:
         _check(lib().fo_consume_group(
             self._h, _ptr(send, numel=self.mn, itemsize=2, name="send"),
             _ptr(peer, numel=self.mn, itemsize=2, name="peer"), _ptr(recv, numel=self.mn, itemsize=2, name="recv"),
-            _ptr(sig, numel=2 * self.P, itemsize=4, name="sig"), int(epoch), int(g_begin), int(g_end),
+            _ptr(sig, numel=self.sig_words, itemsize=4, name="sig"), int(epoch), int(g_begin), int(g_end),
             _ptr(status, numel=1, itemsize=4, name="status"), int(timeout_us), int(num_workgroups),
             _ptr(trace, numel=self.P, itemsize=8, name="trace"), _stream(stream)), "fo_consume_group")
 

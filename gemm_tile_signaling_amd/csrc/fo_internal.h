@@ -92,6 +92,11 @@ struct fo_plan {
   const int32_t *d_row_dest = nullptr;
   const int32_t *d_row_rank = nullptr;
 
+  // Signal words: cnt[P] at word 0, flag[P] from the next multiple of 64 words,
+  // so the lines consumers poll are not the lines every tile's atomic updates.
+  int32_t flag_offset() const { return (P + 63) / 64 * 64; }
+  int32_t sig_words() const { return flag_offset() + P; }
+
   fo::Layout layout(bool device_side) const {
     fo::Layout L{};
     L.mode = mode == FO_MODE_SUBTOKEN ? fo::kSubtoken : fo::kBanded;

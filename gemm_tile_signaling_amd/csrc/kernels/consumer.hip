@@ -143,7 +143,7 @@ int launch_consume(const fo_plan *p, const void *send, const void *peer, void *r
   cp.send = static_cast<const uint16_t *>(send);
   cp.peer = static_cast<const uint16_t *>(peer);
   cp.recv = static_cast<uint16_t *>(recv);
-  cp.flag = sig + p->P;
+  cp.flag = sig + p->flag_offset();
   cp.unit_off = p->d_unit_off;
   cp.group_unit = p->d_group_unit;
   cp.status = status;

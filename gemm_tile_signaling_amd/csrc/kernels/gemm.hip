@@ -425,7 +425,7 @@ int launch_gemm(const fo_plan *p, const void *A, const void *B, void *Cout, bool
   gp.L = p->layout(true);
   if (rowmajor) gp.L.mode = kRowMajor;
   gp.cnt = sig;
-  gp.flag = sig ? sig + p->P : nullptr;
+  gp.flag = sig ? sig + p->flag_offset() : nullptr;
   gp.thr = p->d_group_tiles;
   gp.trace = sig ? trace : nullptr;
   gp.epoch = epoch;

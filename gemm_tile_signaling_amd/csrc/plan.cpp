@@ -326,6 +326,8 @@ int fo_plan_info_get(const fo_plan *p, fo_plan_info *o) {
   o->num_problems = p->num_problems;
   o->device = p->host_only ? -1 : p->device;
   o->clock_khz = p->host_only ? 0 : (int32_t)(p->ticks_per_us * 1000u);
+  o->sig_words = p->sig_words();
+  o->flag_offset = p->flag_offset();
   return FO_OK;
 }
 

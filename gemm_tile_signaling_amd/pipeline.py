@@ -13,7 +13,8 @@ streams that shared a queue would complete (serialised, without overlap).
 
 Buffers (torch tensors, 16-bit elements stored as int16):
   A [M*K], B [problems*N*K], reorder_buf / peer / recv / out [M*N],
-  sig int32 [2P] (zeroed once; epochs count up), status int32 [1].
+  sig int32 [sig_words] (cnt[P], then flag[P] from flag_offset; zeroed once;
+  epochs count up), status int32 [1].
 """
 
 from __future__ import annotations
@@ -35,7 +36,7 @@ class Pipeline:
         self.buf = torch.empty(n, dtype=torch.int16, device=dev)
         self.recv = self.buf if in_place else torch.empty(n, dtype=torch.int16, device=dev)
         self.out = torch.empty(n, dtype=torch.int16, device=dev)
-        self.sig = torch.zeros(max(1, 2 * plan.P), dtype=torch.int32, device=dev)
+        self.sig = plan.new_sig(dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         # each side gets a hardware queue of its own, or the consumer would run after the GEMM
         with torch.cuda.device(dev):

@@ -112,6 +112,8 @@ typedef struct fo_plan_info {
   int32_t mode, ranks, dtype, num_problems;
   int32_t device;                  /* HIP device the tables live on; -1 if host-only          */
   int32_t clock_khz;               /* rate of the device wall clock used by the traces; 0 if host-only */
+  int32_t sig_words;               /* uint32 words of the signal buffer: flag_offset + P      */
+  int32_t flag_offset;             /* word index of flag[0]: P rounded up to a multiple of 64 */
 } fo_plan_info;
 
 /*
@@ -161,8 +163,11 @@ int fo_plan_offsets(const fo_plan *plan, int64_t *off);
  * cnt[group], and -- by the tile that brings cnt[group] to epoch*|G_group|
  * -- a release store flag[group] = epoch.
  *
- * sig: device uint32[2*P] = cnt[P] followed by flag[P]; zero it once before
- *      the first epoch.  Epochs start at 1 and increase by 1 per launch on
+ * sig: device uint32[sig_words] (fo_plan_info): the counting table cnt[P] at
+ *      word 0 and the flags flag[P] at word flag_offset, the first multiple of
+ *      64 words (256 bytes) at or after P, so that with a 256-byte aligned sig
+ *      the flags that consumers poll never share a cache line with the
+ *      counters every tile increments.  Zero it once before the first epoch.  Epochs start at 1 and increase by 1 per launch on
  *      the same sig, so no reset is needed between launches; after epoch e,
  *      cnt[j] == e*|G_j|.  epoch * max|G_j| must fit in 32 bits.
  * trace: NULL, or device uint64[2*NT + P]: for slot s, trace[2s] = wall
@@ -181,9 +186,11 @@ int fo_gemm_plain(const fo_plan *plan, const void *A, const void *B, void *C, hi
 
 /*
  * Consumer: for groups g = g_begin .. g_end-1 in order, wait on the device
- * until flag[g] >= epoch, then for every unit of g compute
+ * until flag[g] >= epoch (sig laid out as for fo_gemm_signal), then for every
+ * unit of g compute
  *   recv[u] = round(float(send[u]) + float(peer[u]))   (element type, RNE)
- * over the unit's elements.  send, peer, recv are flat M*N buffers in the
+ * over the unit's elements (the units of a group tile its span, so the
+ * kernel streams the span in one pass).  send, peer, recv are flat M*N buffers in the
  * reordered layout; recv may equal send.  This stands in for the group's
  * collective call on the contiguous span (deep-dive 二 › (1) code box;
  * 五 › 专用监控内核).

@@ -72,3 +72,16 @@ def test_default_plan_parameters():
     p = fo.Plan(2048, 8192, 8192, host_only=True)
     assert (p.BM, p.BN, p.S, p.W) == (256, 128, 4, 256)
     assert p.NT == 512 and p.T == 2 and p.P == 2
+
+
+def test_signal_buffer_layout():
+    """cnt[P] from word 0, flag[P] from the next multiple of 64 words (a 256-byte boundary)."""
+    P = fo.Plan
+    p = P(256, 256, 64, "fp16", BM=64, BN=64, swizzle=2, wave_size=4, composition=(1, 2, 1), host_only=True)
+    assert (p.P, p.flag_offset, p.sig_words) == (3, 64, 67)
+    many = P(64 * 80, 64, 64, BM=64, BN=64, swizzle=1, wave_size=1, host_only=True)   # one wave per group
+    assert (many.P, many.flag_offset, many.sig_words) == (80, 128, 208)
+    edge = P(64 * 64, 64, 64, BM=64, BN=64, swizzle=1, wave_size=1, host_only=True)
+    assert (edge.P, edge.flag_offset, edge.sig_words) == (64, 64, 128)
+    empty = P(0, 64, 64, BM=64, BN=64, swizzle=1, wave_size=4, composition=(), host_only=True)
+    assert (empty.P, empty.flag_offset, empty.sig_words) == (0, 0, 0)

@@ -92,8 +92,8 @@ def test_consumer_all_groups_bit_exact(entry):
     peer = random_bits(12, o.M * o.N, dt)
     want = oracle.consume_add(send, peer, dt)
     say(f"consumer {entry[0]} P={o.P} units={p.num_units}")
-    sig = zeros_i32(2 * p.P)
-    sig[p.P:] = 3                      # every group already signalled at epoch 3
+    sig = p.new_sig()
+    p.flag_of(sig).fill_(3)            # every group already signalled at epoch 3
     status = zeros_i32(1)
     dsend, dpeer = to_dev(send), to_dev(peer)
     recv = empty16(o.M * o.N)
@@ -116,9 +116,8 @@ def test_consumer_times_out_on_unsignalled_group_and_leaves_it_untouched():
     want = oracle.consume_add(send, peer, dt)
     spans = group_spans(o)
     say("consumer time-out: group 2 never signalled, 20 ms limit")
-    sig = zeros_i32(2 * p.P)
-    sig[p.P + 0] = 1
-    sig[p.P + 1] = 1                   # group 2 stays at 0: the host never raises it
+    sig = p.new_sig()
+    p.flag_of(sig)[0:2] = 1            # group 2 stays at 0: the host never raises it
     status = zeros_i32(1)
     recv = empty16(o.M * o.N)
     p.consume_group(to_dev(send), to_dev(peer), recv, sig, 1, status, timeout_us=20000, num_workgroups=4)
@@ -137,8 +136,8 @@ def test_consumer_group_range():
     want = oracle.consume_add(send, peer, "bf16")
     spans = group_spans(o)
     say("consumer groups [1, 3)")
-    sig = zeros_i32(2 * p.P)
-    sig[p.P:] = 1
+    sig = p.new_sig()
+    p.flag_of(sig).fill_(1)
     status = zeros_i32(1)
     recv = empty16(o.M * o.N)
     p.consume_group(to_dev(send), to_dev(peer), recv, sig, 1, status, g_begin=1, g_end=3)
@@ -175,7 +174,7 @@ def test_gemm_ternary_bit_exact(entry):
     say(f"gemm ternary {entry[0]}")
     C = empty16(o.M * o.N)
     buf = empty16(o.M * o.N)
-    sig = zeros_i32(2 * p.P)
+    sig = p.new_sig()
     dA, dB = to_dev(A), to_dev(_stack(B))
     p.gemm_plain(dA, dB, C)
     p.gemm_signal(dA, dB, buf, sig, 1)
@@ -195,7 +194,7 @@ def test_gemm_signal_tables_and_layout(entry):
     C = empty16(o.M * o.N)
     buf = empty16(o.M * o.N)
     back = empty16(o.M * o.N)
-    sig = zeros_i32(2 * p.P)
+    sig = p.new_sig()
     trace = torch.zeros(2 * p.NT + p.P, dtype=torch.int64, device="cuda")
     p.gemm_plain(dA, dB, C)
     for epoch in (1, 2, 3):
@@ -204,7 +203,8 @@ def test_gemm_signal_tables_and_layout(entry):
         torch.cuda.synchronize()
         s = sig.cpu().numpy()
         assert s[:p.P].tolist() == [epoch * g for g in o.group_tiles]          # counting table
-        assert s[p.P:].tolist() == [epoch] * p.P                               # every group signalled
+        assert s[p.flag_offset:p.flag_offset + p.P].tolist() == [epoch] * p.P  # every group signalled
+        assert not s[p.P:p.flag_offset].any()                                 # padding untouched
         tr = trace.cpu().numpy().view(np.uint64)
         tickets = (tr[1:2 * p.NT:2] & 0xFFFFFFFF).astype(np.int64)
         for j in range(p.P):
@@ -227,7 +227,7 @@ def test_gemm_each_workgroup_runs_its_wave_slot():
     o, p = _plans(entry)
     A, B, _ = _inputs(entry)
     say("gemm_signal wave placement W=4")
-    sig = zeros_i32(2 * p.P)
+    sig = p.new_sig()
     trace = torch.zeros(2 * p.NT + p.P, dtype=torch.int64, device="cuda")
     buf = empty16(o.M * o.N)
     p.gemm_signal(to_dev(A), to_dev(_stack(B)), buf, sig, 1, trace=trace)
@@ -283,7 +283,7 @@ def test_every_kernel_with_buffers_above_bit31_of_the_low_word():
     X.copy_(to_dev(Xh).reshape(-1))
     for v in (C, buf, recv, out, Y):
         v.fill_(0x7FC0)
-    sig = zeros_i32(2 * p.P)
+    sig = p.new_sig()
     status = zeros_i32(1)
     p.gemm_plain(dA, dB, C)
     p.gemm_signal(dA, dB, buf, sig, 1)

@@ -38,7 +38,7 @@ def test_pipeline_matches_oracle(entry, in_place):
     assert int(pipe.status.item()) == 0
     s = pipe.sig.cpu().numpy()
     assert s[:p.P].tolist() == [3 * g for g in o.group_tiles]
-    assert s[p.P:].tolist() == [3] * p.P
+    assert s[p.flag_offset:p.flag_offset + p.P].tolist() == [3] * p.P
     out = to_host(pipe.out).reshape(o.M, o.N)
     tol_check_out(out, want_out, r["C64"], dt, "out")
     # the oracle's own end-to-end result agrees with its definition

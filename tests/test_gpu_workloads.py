@@ -80,7 +80,7 @@ def test_workload_full_size(name, comp):
     assert int(pipe.status.item()) == 0
     sg = pipe.sig.cpu().numpy()
     assert sg[:p.P].tolist() == [2 * g for g in o.group_tiles]
-    assert sg[p.P:].tolist() == [2] * p.P
+    assert sg[p.flag_offset:p.flag_offset + p.P].tolist() == [2] * p.P
     out = to_host(pipe.out).reshape(o.M, o.N)
     want_out = oracle.decode_bits(s["out"], w.dtype)
     tol_check_out(out[rows, cols], want_out, s["C64"], w.dtype, "out (sampled)")
