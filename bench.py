@@ -41,6 +41,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="profiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-search", action="store_true",
+                    help="skip the check of the predictive partition search against measured partitions")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc passes: the calibration copy and each kernel launched alone on one "
                          "stream (counter collection serialises dispatches, which the two-stream pipeline "
@@ -54,6 +56,87 @@ def _event_pairs(torch, n):
 
 def _flush_mall(torch, scratch):
     scratch.fill_(1)        # writes 512 MiB: evicts the 256 MB memory-side cache
+
+
+def search_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
+    """Predictive partition search against measurement on the 4-wave prefill workload.
+
+    The search's offline inputs, as the pages describe them (deep-dive
+    四 › 离线阶段 / 在线阶段): the GEMM's duration (the plain GEMM alone) and a
+    latency-versus-size curve of the communication -- here its one-GPU
+    stand-in, the consumer, run on a single group of each sampled size with
+    the flag already raised (HIP events, so a call's fixed cost is included).
+    fo_plan_search scores all 2^(T-1) partitions; every partition then runs in
+    the pipeline, and the measured end of communication (GEMM start to the
+    consumer's end) is set against the prediction.
+    """
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["ar_prefill"]
+    A, B, peer, m_per, rd = make_inputs(w)
+    dA = torch.from_numpy(A.view(np.int16).reshape(-1).copy()).to(dev)
+    dB = torch.from_numpy(np.concatenate([b.reshape(-1) for b in B]).view(np.int16).copy()).to(dev)
+    dpeer = torch.from_numpy(peer.view(np.int16).copy()).to(dev)
+    s = torch.cuda.Stream(device=dev)
+    base = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W)
+    C = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
+    gemm_ms = float(np.median([_time_kernel(torch, lambda st: base.gemm_plain(dA, dB, C, stream=st), s, 1)
+                               for _ in range(10)]))
+    curve_b, curve_s = [], []
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for rows in (16, 64, 256, 1024, 2048, 4096):
+        cp = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W)
+        cp = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=(cp.T,))
+        x = torch.zeros(cp.M * cp.N, dtype=torch.int16, device=dev)
+        y = torch.empty_like(x)
+        ready = cp.new_sig(dev)
+        cp.flag_of(ready).fill_(1)
+        ms = float(np.median([_time_kernel(torch, lambda st: cp.consume_group(x, x, y, ready, 1, status, stream=st),
+                                           s, 1) for _ in range(10)]))
+        curve_b.append(2.0 * cp.M * cp.N)
+        curve_s.append(ms * 1e-3)
+    pred, pred_s, all_s = base.search(gemm_ms * 1e-3, curve_b, curve_s, with_all=True)
+
+    def comp_of(mask, T):     # cut mask -> waves per group (bit i: a group ends after wave i+1)
+        out, run = [], 0
+        for wv in range(T):
+            run += 1
+            if wv == T - 1 or (mask >> wv) & 1:
+                out.append(run)
+                run = 0
+        return tuple(out)
+
+    rows = []
+    for mask in range(1 << (base.T - 1)):
+        comp = comp_of(mask, base.T)
+        plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp)
+        pipe = Pipeline(plan, dA, dB, dpeer)
+        for _ in range(warmup):
+            pipe.step()
+        evs = [{k: _event_pairs(torch, 1)[0] for k in ("gemm", "consume", "post")} for _ in range(steps)]
+        for e in evs:
+            pipe.step(events=e)
+        pipe.join()
+        torch.cuda.synchronize()
+        if int(pipe.status.item()) != 0:
+            raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
+        meas = float(np.median([e["gemm"][0].elapsed_time(e["consume"][1]) for e in evs]))
+        pipe.close()
+        rows.append((comp, all_s[mask] * 1e3, meas))
+    best_m = min(rows, key=lambda r: r[2])
+    pick = next(r for r in rows if r[0] == pred)
+    order = sorted(rows, key=lambda r: r[2])
+    return {
+        "workload": f"{w.name}: M={w.M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, wave {w.W}, T={base.T}",
+        "gemm_plain_us": round(gemm_ms * 1e3, 1),
+        "curve_bytes": curve_b, "curve_us": [round(x * 1e6, 2) for x in curve_s],
+        "predicted_best": list(pred), "predicted_us": round(pred_s * 1e6, 1),
+        "measured_best": list(best_m[0]), "measured_best_us": round(best_m[2] * 1e3, 1),
+        "predicted_choice_measured_us": round(pick[2] * 1e3, 1),
+        "regret": round(pick[2] / best_m[2] - 1.0, 4),
+        "rank_of_predicted_choice": 1 + [r[0] for r in order].index(pred),
+        "candidates": [{"groups": list(c), "predicted_us": round(p * 1e3, 1), "measured_us": round(m * 1e3, 1)}
+                       for c, p, m in rows],
+    }
 
 
 def _time_kernel(torch, launch, stream, n, scratch=None):
@@ -272,6 +355,8 @@ def main():
                         "post_ms": round(r["post_ms"], 4)} for r in results],
         "cpu_baseline": None,
     }
+    if not a.no_search:
+        line["search"] = search_check(torch, fo, Pipeline, dev)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, peer, m_per, row_dest, best["comp"])
     print(json.dumps(line), flush=True)

@@ -75,6 +75,7 @@ def lib() -> C.CDLL:
             "fo_plan_tables": [vp, vp, vp, vp, vp, vp],
             "fo_plan_units": [vp, vp, vp],
             "fo_plan_offsets": [vp, vp],
+            "fo_plan_search": [vp, C.c_double, vp, vp, i32, vp, vp, vp, vp],
             "fo_gemm_signal": [vp, vp, vp, vp, vp, u32, vp, vp],
             "fo_gemm_plain": [vp, vp, vp, vp, vp],
             "fo_consume_group": [vp, vp, vp, vp, vp, u32, i32, i32, vp, u64, i32, vp, vp],
@@ -209,6 +210,22 @@ class Plan:
         off = np.full((self.M, self.N), -1, np.int64)
         _check(lib().fo_plan_offsets(self._h, off.ctypes.data if off.size else None), "fo_plan_offsets")
         return off
+
+    def search(self, gemm_seconds: float, curve_bytes, curve_seconds, with_all: bool = False):
+        """Predictive partition search (``fo_plan_search``): returns (composition, predicted
+        seconds, every candidate's prediction in cut-mask order or None)."""
+        cb = np.ascontiguousarray(curve_bytes, dtype=np.float64)
+        cs = np.ascontiguousarray(curve_seconds, dtype=np.float64)
+        if cb.shape != cs.shape or cb.ndim != 1:
+            raise ValueError("curve_bytes and curve_seconds must be 1-D and of one length")
+        best = np.zeros(max(1, self.T), np.int32)
+        ng = C.c_int32()
+        bt = C.c_double()
+        allt = np.zeros(1 << (self.T - 1), np.float64) if with_all and 0 < self.T <= 24 else None
+        _check(lib().fo_plan_search(self._h, float(gemm_seconds), cb.ctypes.data, cs.ctypes.data, int(cb.size),
+                                    best.ctypes.data, C.byref(ng), C.byref(bt),
+                                    allt.ctypes.data if allt is not None else None), "fo_plan_search")
+        return tuple(int(x) for x in best[:ng.value]), bt.value, allt
 
     # ------------------------------------------------------------------ enqueue calls
     @property

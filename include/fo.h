@@ -156,6 +156,31 @@ int fo_plan_units(const fo_plan *plan, int64_t *unit_off, int32_t *group_unit);
 int fo_plan_offsets(const fo_plan *plan, int64_t *off);
 
 /*
+ * Predictive partition search (deep-dive 四、实时调优 › 在线阶段: 预测搜索算法,
+ * Algorithm 1).  Scores every composition of the plan's T waves -- 2^(T-1)
+ * candidates; the plan's own composition is not used -- with the pages'
+ * latency model and returns the best:
+ *   for each group i in order:
+ *     t_acc_m = max(t_acc_p, t_acc_m) + lat(bytes of group i-1)   (0 for i = 0)
+ *     t_acc_p = t_acc_p + gemm_seconds / T * (waves of group i)
+ *   prediction = max(t_acc_p, t_acc_m) + lat(bytes of the last group)
+ * bytes of a group = its span (elements x 2).  lat() interpolates the
+ * sampled curve (curve_bytes[points] > 0, strictly increasing;
+ * curve_seconds[points] >= 0) linearly, holds the first sample's latency
+ * below it, grows at the last sample's bandwidth beyond it, and is 0 for
+ * 0 bytes.  gemm_seconds >= 0 is the whole GEMM's duration.
+ * best_comp: host int32[T], receives the winning composition
+ *   (*best_num_groups entries); ties keep the first candidate in mask order.
+ * all_seconds: NULL or host double[2^(T-1)]: the prediction of candidate
+ *   `mask` (bit i set = a group ends after wave i+1) at index mask.
+ * Errors: FO_ERR_INVALID for a malformed curve or NULL outputs,
+ *   FO_ERR_UNSUPPORTED for T > 24.  Host-only plans are accepted.
+ */
+int fo_plan_search(const fo_plan *plan, double gemm_seconds, const double *curve_bytes,
+                   const double *curve_seconds, int32_t points, int32_t *best_comp,
+                   int32_t *best_num_groups, double *best_seconds, double *all_seconds);
+
+/*
  * Signaling GEMM (deep-dive 五 › 扩展主循环 and Epilogue 集成): C = A . B^T
  * with every finished tile stored through the mapping table into
  * `reorder_buf` (M*N elements, the contiguous per-group spans), followed by

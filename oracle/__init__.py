@@ -16,7 +16,7 @@ section:
   abstract and figure captions).
 
 Where the pages leave a step open, the oracle takes one plain reading; each
-reading is listed in the design doc and named in the docstring that uses it.
+reading is named in the docstring of the function that takes it.
 
 Modules
 -------

@@ -15,7 +15,7 @@ Written from the deep-dive page "FlashOverlap: 信号驱动计算通信重叠论
 * the code box under 二 shows the execution order [t0, t3, t1, t2] sent to
   reorder indices 0, 1, 2, 3 and back.
 
-Readings (the design doc lists them):
+Readings:
 
 * reorder indices ("slots") follow dispatch order, so each group occupies a
   consecutive run of slots;

@@ -1,7 +1,7 @@
 """Floating-point steps of the path, in fp64, for the oracle (test infrastructure only).
 
 The pages fix no precision for the GEMM or for the data that the collective
-moves.  Readings (listed in the design doc):
+moves.  Readings:
 
 * the GEMM's inputs and output are in the model's 16-bit type (bf16 or fp16)
   and the product is accumulated in high precision; the oracle accumulates in

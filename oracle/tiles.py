@@ -14,7 +14,7 @@ Oracle, test infrastructure only.  Written from the deep-dive page
 * 三、Wave Group 划分设计空间 › 设计空间大小 (after every wave but the last
   one may communicate or not: 2^(T-1) partitions).
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 
 * swizzle: grouped-M order of width S (bands of S tile rows, walked column
   by column inside a band); S = 1 is row-major order;
