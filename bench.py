@@ -58,6 +58,29 @@ def _flush_mall(torch, scratch):
     scratch.fill_(1)        # writes 512 MiB: evicts the 256 MB memory-side cache
 
 
+def wave_pattern_of(t_sig, W, tick_us, bins=40):
+    """Tile completion times grouped by wave (deep-dive 三 › wave 模式; the summary page's wave figure).
+
+    t_sig[s] is the device wall clock at slot s's signal; slot s belongs to
+    wave s // W.  Times are relative to the first signal of the launch.
+    Returns each wave's first / median / last completion, the gap between
+    the end of one wave and the start of the next, and a histogram of
+    completions per wave over the launch.
+    """
+    t = (np.asarray(t_sig, dtype=np.int64) - int(np.min(t_sig))) * tick_us
+    T = (len(t) + W - 1) // W
+    per = []
+    for wv in range(T):
+        x = t[wv * W:(wv + 1) * W]
+        per.append({"tiles": int(x.size), "first_us": round(float(x.min()), 2),
+                    "median_us": round(float(np.median(x)), 2), "last_us": round(float(x.max()), 2)})
+    edges = np.linspace(0.0, float(t.max()) + 1e-9, bins + 1)
+    hist = [np.histogram(t[wv * W:(wv + 1) * W], bins=edges)[0].tolist() for wv in range(T)]
+    return {"waves": per,
+            "gap_us": [round(per[i + 1]["first_us"] - per[i]["last_us"], 2) for i in range(T - 1)],
+            "bin_us": round(float(edges[1] - edges[0]), 3), "histogram": hist}
+
+
 def search_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
     """Predictive partition search against measurement on the 4-wave prefill workload.
 
@@ -297,6 +320,7 @@ def main():
     last = np.array([t_sig[grp == j].max() for j in range(plan.P)])
     signal_to_consume_us = [round(float(x) * tick_us, 2) for x in (c - last)]
     first_consume_before_gemm_end_us = round(float(last[-1] - c[0]) * tick_us, 2)
+    wave_pattern = wave_pattern_of(t_sig, plan.W, tick_us)
 
     # kernels alone (same plan), each timed with HIP events on its own stream
     s = torch.cuda.Stream(device=dev)
@@ -350,6 +374,7 @@ def main():
         "post_reorder_frac_hbm": round(post_gbps / PEAK_HBM_GBPS, 4),
         "signal_to_consume_us": signal_to_consume_us,
         "first_group_consumed_before_gemm_end_us": first_consume_before_gemm_end_us,
+        "wave_pattern": wave_pattern,
         "partitions": [{"groups": list(r["comp"]), "step_ms": round(r["step_ms"], 4),
                         "gemm_ms": round(r["gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
                         "post_ms": round(r["post_ms"], 4)} for r in results],
