@@ -341,6 +341,10 @@ def main():
     consume_ms = _time_kernel(torch, lambda st: plan.consume_group(pipe.buf, dpeer, recv, ready, 1, status, stream=st),
                               s, n_alone, scratch)
     post_ms = _time_kernel(torch, lambda st: plan.reorder_post(recv, C, stream=st), s, n_alone, scratch)
+    bias = (torch.randn(plan.num_problems * w.N, device=dev) * 0.02).to(torch.bfloat16 if w.dtype == "bf16"
+                                                                        else torch.float16).view(torch.int16)
+    post_ep_ms = _time_kernel(torch, lambda st: plan.reorder_post_ep(recv, C, bias=bias, act="silu", stream=st), s,
+                              n_alone, scratch)
     mn = w.M * w.N
     consume_gbps = 6.0 * mn / (consume_ms * 1e-3) / 1e9
     post_gbps = 4.0 * mn / (post_ms * 1e-3) / 1e9
@@ -370,6 +374,8 @@ def main():
         "signal_with_consumer_over_plain": round(plain_ms / best["gemm_ms"], 4),
         "consumer_alone_gbps": round(consume_gbps, 1),
         "post_reorder_alone_gbps": round(post_gbps, 1),
+        "post_reorder_bias_silu_alone_gbps": round((4.0 * mn + 2.0 * plan.num_problems * w.N) / (post_ep_ms * 1e-3) / 1e9,
+                                                   1),
         "consumer_frac_hbm": round(consume_gbps / PEAK_HBM_GBPS, 4),
         "post_reorder_frac_hbm": round(post_gbps / PEAK_HBM_GBPS, 4),
         "signal_to_consume_us": signal_to_consume_us,

@@ -9,8 +9,9 @@ buffer.
 
 The names follow the C ABI in ``include/fo.h``: ``Plan`` wraps
 ``fo_plan_groups``; its methods ``gemm_signal``, ``gemm_plain``,
-``consume_group``, ``reorder_post`` and ``reorder_pre`` wrap the enqueue
-calls of the same names.
+``consume_group``, ``reorder_post``, ``reorder_post_ep`` and ``reorder_pre``
+wrap the enqueue calls of the same names, and ``search`` wraps
+``fo_plan_search``.
 """
 
 from __future__ import annotations
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
 FO_OK, FO_ERR_INVALID, FO_ERR_UNSUPPORTED, FO_ERR_HIP, FO_ERR_NOMEM, FO_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
 _DTYPES = {"bf16": 0, "fp16": 1}
 _MODES = {"tile": 0, "subtile": 1, "subtoken": 2}
+_ACTS = {"none": 0, "relu": 1, "silu": 2}
 FO_PLAN_HOST_ONLY = 1
 
 
@@ -83,6 +85,7 @@ def lib() -> C.CDLL:
             "fo_stream_destroy": [vp],
             "fo_reorder_post": [vp, vp, vp, vp],
             "fo_reorder_pre": [vp, vp, vp, vp],
+            "fo_reorder_post_ep": [vp, vp, vp, vp, i32, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -275,6 +278,13 @@ class Plan:
         _check(lib().fo_reorder_post(self._h, _ptr(reordered, numel=self.mn, itemsize=2, name="reordered"),
                                      _ptr(out, numel=self.mn, itemsize=2, name="out"), _stream(stream)),
                "fo_reorder_post")
+
+    def reorder_post_ep(self, reordered, out, bias=None, act: str = "none", stream=None):
+        """Post-communication reorder fused with bias + activation (``fo_reorder_post_ep``)."""
+        _check(lib().fo_reorder_post_ep(self._h, _ptr(reordered, numel=self.mn, itemsize=2, name="reordered"),
+                                        _ptr(out, numel=self.mn, itemsize=2, name="out"),
+                                        _ptr(bias, numel=self.num_problems * self.N, itemsize=2, name="bias"),
+                                        _ACTS[act], _stream(stream)), "fo_reorder_post_ep")
 
     def reorder_pre(self, rowmajor, reordered, stream=None):
         _check(lib().fo_reorder_pre(self._h, _ptr(rowmajor, numel=self.mn, itemsize=2, name="in"),

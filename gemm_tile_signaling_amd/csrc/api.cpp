@@ -64,6 +64,15 @@ int fo_reorder_post(const fo_plan *p, const void *reordered, void *out, hipStrea
   return fo::launch_reorder(p, reordered, out, true, stream);
 }
 
+int fo_reorder_post_ep(const fo_plan *p, const void *reordered, void *out, const void *bias, int32_t act,
+                       hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (!buf_ok(p, reordered) || !buf_ok(p, out)) return FO_ERR_INVALID;
+  if (bias && !aligned16(bias)) return FO_ERR_INVALID;
+  if (act != FO_ACT_NONE && act != FO_ACT_RELU && act != FO_ACT_SILU) return FO_ERR_INVALID;
+  return fo::launch_post_ep(p, reordered, out, bias, act, stream);
+}
+
 int fo_reorder_pre(const fo_plan *p, const void *in, void *reordered, hipStream_t stream) {
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (!buf_ok(p, in) || !buf_ok(p, reordered)) return FO_ERR_INVALID;

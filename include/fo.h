@@ -62,6 +62,13 @@ typedef enum fo_mode {
                             destination; a group's span holds `ranks` buckets              */
 } fo_mode;
 
+/* Element-wise activation of the fused post-reorder epilogue. */
+typedef enum fo_act {
+  FO_ACT_NONE = 0,
+  FO_ACT_RELU = 1,   /* max(x, 0)            */
+  FO_ACT_SILU = 2,   /* x / (1 + exp(-x))    */
+} fo_act;
+
 /* Plan flags. */
 #define FO_PLAN_HOST_ONLY 0x1u   /* build the tables on the host only; enqueue calls reject the plan */
 
@@ -240,6 +247,20 @@ int fo_consume_group(const fo_plan *plan, const void *send, const void *peer, vo
 
 /* Post-communication reordering: out[m*N + n] = reordered[off(m, n)] (inverse mapping). */
 int fo_reorder_post(const fo_plan *plan, const void *reordered, void *out, hipStream_t stream);
+
+/*
+ * Post-communication reordering fused with the element-wise epilogue
+ * (deep-dive 五 › Epilogue 集成: the operations that follow the GEMM -- bias
+ * addition, ReLU, SiLU -- run in the reorder's pass, so the output is
+ * written once):
+ *   out[m*N + n] = round(act(float(reordered[off(m, n)]) + float(bias[e(m)*N + n])))
+ * e(m) is the problem (expert) row m belongs to; bias: NULL (no bias) or
+ * device, 16-byte aligned, num_problems * N elements of the plan's type.
+ * act: fo_act.  One fp32 addition, the activation in fp32, one rounding to
+ * nearest even.  reordered and out as for fo_reorder_post.
+ */
+int fo_reorder_post_ep(const fo_plan *plan, const void *reordered, void *out, const void *bias, int32_t act,
+                       hipStream_t stream);
 
 /* Pre-communication reordering as a separate pass: reordered[off(m, n)] = in[m*N + n]. */
 int fo_reorder_pre(const fo_plan *plan, const void *in, void *reordered, hipStream_t stream);

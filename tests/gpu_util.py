@@ -79,3 +79,15 @@ def tol_check_out(gpu_bits, want_out, c_ref, dtype: str, what: str):
         i = int(np.argmax(bad.ravel()))
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the derived bound; first at {i}: "
                              f"gpu {g.ravel()[i]!r} oracle {r.ravel()[i]!r} C {c.ravel()[i]!r}")
+
+
+def ulp_distance(a_bits, b_bits) -> np.ndarray:
+    """Distance in units of the last place between two arrays of bf16/fp16 patterns.
+
+    Both types order their finite values by the sign-magnitude integer of the
+    pattern, so adjacent values differ by one; +0 and -0 are the same point.
+    """
+    def key(x):
+        x = np.asarray(x, dtype=np.uint16).astype(np.int64)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(key(a_bits) - key(b_bits))

@@ -12,7 +12,8 @@ import pytest
 import oracle
 from oracle.layout import element_offsets, group_spans
 from oracle.tiles import make_plan
-from tests.gpu_util import empty16, say, to_dev, to_host, tol_check, tol_check_out, zeros_i32
+from oracle.epilogue import post_epilogue, row_problems
+from tests.gpu_util import empty16, say, to_dev, to_host, tol_check, tol_check_out, ulp_distance, zeros_i32
 from workloads import draw, random_bits, to_bits
 
 pytestmark = pytest.mark.gpu
@@ -80,6 +81,33 @@ def test_reorder_pre_post_bit_exact(entry):
     torch.cuda.synchronize()
     assert np.array_equal(to_host(r1), want_pre)
     assert np.array_equal(to_host(r2), want_post)
+
+
+# --------------------------------------------------------------------------- fused post-reorder epilogue
+
+@pytest.mark.parametrize("act", ["none", "relu", "silu"])
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_post_reorder_epilogue(entry, act):
+    """none / relu: bit-exact (one fp32 add, one rounding on both sides); silu: within one
+    unit in the last place (the kernel evaluates exp in fp32, the oracle in fp64)."""
+    o, p = _plans(entry)
+    dt = entry[4]
+    off = element_offsets(o)
+    Y = to_bits(draw(61, (o.M * o.N,), ("normal", 2.0)), dt)
+    bias = to_bits(draw(62, (len(o.m_per_problem) * o.N,), ("normal", 1.0)), dt)
+    dY = to_dev(Y)
+    for b in (None, bias):
+        want = post_epilogue(Y, off, dt, act, b, row_problems(o)).ravel()
+        say(f"post epilogue {entry[0]} act={act} bias={b is not None}")
+        out = empty16(o.M * o.N)
+        p.reorder_post_ep(dY, out, bias=to_dev(b) if b is not None else None, act=act)
+        torch.cuda.synchronize()
+        got = to_host(out)
+        if act == "silu":
+            d = ulp_distance(got, want)
+            assert d.max() <= 1, (int(d.max()), int((d > 0).sum()))
+        else:
+            assert np.array_equal(got, want)
 
 
 # --------------------------------------------------------------------------- consumer
