@@ -80,6 +80,7 @@ def lib() -> C.CDLL:
             "fo_plan_search": [vp, C.c_double, vp, vp, i32, vp, vp, vp, vp],
             "fo_gemm_signal": [vp, vp, vp, vp, vp, u32, vp, vp],
             "fo_gemm_plain": [vp, vp, vp, vp, vp],
+            "fo_gemm_signal_serialized": [vp, vp, vp, vp, vp, u32, vp, vp],
             "fo_consume_group": [vp, vp, vp, vp, vp, u32, i32, i32, vp, u64, i32, vp, vp],
             "fo_stream_create": [C.POINTER(vp)],
             "fo_stream_destroy": [vp],
@@ -257,6 +258,17 @@ class Plan:
             _ptr(reorder_buf, numel=self.mn, itemsize=2, name="reorder_buf"),
             _ptr(sig, numel=self.sig_words, itemsize=4, name="sig"), int(epoch),
             _ptr(trace, numel=2 * self.NT + self.P, itemsize=8, name="trace"), _stream(stream)), "fo_gemm_signal")
+
+    def gemm_signal_serialized(self, A, B, reorder_buf, sig, epoch: int, snapshots, stream=None):
+        """Debug form with a device-wide barrier after every wave (``fo_gemm_signal_serialized``);
+        ``snapshots`` is int32[T*2P + 2], zeroed: row w holds cnt[P] then flag[P] after wave w."""
+        _check(lib().fo_gemm_signal_serialized(
+            self._h, _ptr(A, numel=self.M * self.K, itemsize=2, name="A"),
+            _ptr(B, numel=self.num_problems * self.N * self.K, itemsize=2, name="B"),
+            _ptr(reorder_buf, numel=self.mn, itemsize=2, name="reorder_buf"),
+            _ptr(sig, numel=self.sig_words, itemsize=4, name="sig"), int(epoch),
+            _ptr(snapshots, numel=2 * self.T * self.P + 2, itemsize=4, name="snapshots"), _stream(stream)),
+            "fo_gemm_signal_serialized")
 
     def gemm_plain(self, A, B, Cout, stream=None):
         _check(lib().fo_gemm_plain(

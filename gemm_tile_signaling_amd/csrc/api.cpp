@@ -30,14 +30,27 @@ int fo_gemm_signal(const fo_plan *p, const void *A, const void *B, void *reorder
   int32_t max_g = 0;
   for (int32_t v : p->group_tiles) max_g = v > max_g ? v : max_g;
   if ((uint64_t)epoch * (uint64_t)max_g > 0xFFFFFFFFull) return FO_ERR_INVALID;
-  return fo::launch_gemm(p, A, B, reorder_buf, false, sig, epoch, trace, stream);
+  return fo::launch_gemm(p, A, B, reorder_buf, false, sig, epoch, trace, nullptr, stream);
+}
+
+int fo_gemm_signal_serialized(const fo_plan *p, const void *A, const void *B, void *reorder_buf, uint32_t *sig,
+                              uint32_t epoch, uint32_t *snapshots, hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (p->NT == 0) return FO_OK;
+  if (!A || !B || !aligned16(A) || !aligned16(B) || !buf_ok(p, reorder_buf)) return FO_ERR_INVALID;
+  if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return FO_ERR_INVALID;
+  if (!snapshots || (reinterpret_cast<uintptr_t>(snapshots) & 3u)) return FO_ERR_INVALID;
+  int32_t max_g = 0;
+  for (int32_t v : p->group_tiles) max_g = v > max_g ? v : max_g;
+  if ((uint64_t)epoch * (uint64_t)max_g > 0xFFFFFFFFull) return FO_ERR_INVALID;
+  return fo::launch_gemm(p, A, B, reorder_buf, false, sig, epoch, nullptr, snapshots, stream);
 }
 
 int fo_gemm_plain(const fo_plan *p, const void *A, const void *B, void *C, hipStream_t stream) {
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (p->NT == 0) return FO_OK;
   if (!A || !B || !aligned16(A) || !aligned16(B) || !buf_ok(p, C)) return FO_ERR_INVALID;
-  return fo::launch_gemm(p, A, B, C, true, nullptr, 0, nullptr, stream);
+  return fo::launch_gemm(p, A, B, C, true, nullptr, 0, nullptr, nullptr, stream);
 }
 
 int fo_consume_group(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,

@@ -114,7 +114,7 @@ namespace fo {
 
 // Kernel launchers (the .hip files).  Arguments are validated by the caller.
 int launch_gemm(const fo_plan *p, const void *A, const void *B, void *C, bool rowmajor,
-                uint32_t *sig, uint32_t epoch, uint64_t *trace, hipStream_t s);
+                uint32_t *sig, uint32_t epoch, uint64_t *trace, uint32_t *serial, hipStream_t s);
 int launch_consume(const fo_plan *p, const void *send, const void *peer, void *recv,
                    const uint32_t *sig, uint32_t epoch, int32_t g_begin, int32_t g_end,
                    int32_t *status, uint64_t timeout_ticks, int32_t grid, uint64_t *trace, hipStream_t s);

@@ -136,7 +136,56 @@ struct GemmParams {
   uint64_t *trace;
   uint32_t epoch;
   int32_t P;
+  uint32_t *serial;        // serialized waves only: snapshots [T][2P], then barrier counter, then status
+  uint64_t timeout_ticks;  // serialized waves only: bound on one barrier wait
 };
+
+// Device-wide barrier number k of a cooperative launch: every workgroup arrives
+// once per barrier, so the k-th completes when the arrival count reaches
+// (k + 1) * gridDim.x.  The wait is bounded by the device wall clock: past the
+// bound (or once another workgroup has given up) the status word records
+// FO_ERR_TIMEOUT and every workgroup leaves.  Returns false on a time-out.
+__device__ __forceinline__ bool grid_barrier(uint32_t *bar, uint32_t *status, uint32_t k, uint64_t timeout) {
+  __shared__ int s_ok;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = (k + 1u) * gridDim.x;
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 || wall_clock64() - t0 > timeout) {
+        uint32_t expected = 0;
+        __hip_atomic_compare_exchange_strong(status, &expected, (uint32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_ok = ok;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
+// After wave `w` of a serialized launch: all workgroups meet, workgroup 0
+// copies cnt[P] then flag[P] into snapshot w, and a second barrier keeps every
+// workgroup out of wave w+1 until the copy is taken.
+__device__ __forceinline__ bool wave_snapshot(const GemmParams &p, int w) {
+  const int T = (p.NT + p.W - 1) / p.W;
+  uint32_t *bar = p.serial + 2 * (int64_t)T * p.P, *status = bar + 1;
+  if (!grid_barrier(bar, status, 2u * w, p.timeout_ticks)) return false;
+  if (blockIdx.x == 0) {
+    uint32_t *snap = p.serial + 2 * (int64_t)w * p.P;
+    for (int i = threadIdx.x; i < p.P; i += kThreads) {
+      snap[i] = __hip_atomic_load(&p.cnt[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      snap[p.P + i] = __hip_atomic_load(&p.flag[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  return grid_barrier(bar, status, 2u * w + 1u, p.timeout_ticks);
+}
 
 template <int BM, int BN>
 struct Cfg {
@@ -158,7 +207,12 @@ struct Cfg {
 // SIGNAL: the signaling GEMM (reordered stores, counting table, flags); otherwise
 // the plain GEMM with a row-major epilogue.  Separate instantiations keep the
 // plain kernel free of signaling code and give the two distinct symbols.
-template <typename T, int BM, int BN, bool SIGNAL>
+// SERIAL (with SIGNAL, cooperative launch only): a device-wide barrier after
+// every wave and a snapshot of the signal words, so that the waves are
+// physical and each wave's counting table can be read back; every workgroup
+// then runs exactly T iterations, idling through the tile work of a partial
+// last wave.
+template <typename T, int BM, int BN, bool SIGNAL, bool SERIAL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -193,7 +247,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
   int64_t *rowoff = reinterpret_cast<int64_t *>(smem + C::ROWOFF);
 
-  for (int b = pos; b < p.NT; b += p.W) {
+  const int iters = SERIAL ? (p.NT + p.W - 1) / p.W : 0;
+  for (int b = pos, it = 0; SERIAL ? it < iters : b < p.NT; b += p.W, ++it) {
+    if (SERIAL && b >= p.NT) {  // no tile in this (partial) wave: only the barriers
+      if (!wave_snapshot(p, it)) return;
+      continue;
+    }
     const TileDesc t = p.slots[b];
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)t.row0 * p.K, t.rows * row_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K,
@@ -382,35 +441,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       }
     }
     __syncthreads();  // the next tile's first stage overwrites the staging area
+    if constexpr (SERIAL) {
+      if (!wave_snapshot(p, it)) return;
+    }
   }
 }
 
-template <typename T, int BM, int BN, bool SIGNAL>
-int launch_typed(const GemmParams &gp, hipStream_t s) {
+template <typename T, int BM, int BN, bool SIGNAL, bool SERIAL>
+int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
   using C = Cfg<BM, BN>;
+  const void *fn = reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, SIGNAL, SERIAL>);
   static bool configured = false;  // per process; the attribute is per kernel and device-independent
   if (!configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, SIGNAL>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
-      return FO_ERR_HIP;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess) return FO_ERR_HIP;
     configured = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, SIGNAL>), dim3(gp.W), dim3(kThreads), C::LDS, s, gp);
-  return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
+  if constexpr (SERIAL) {
+    // every workgroup must be resident at once, or the barriers could not complete
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, C::LDS) != hipSuccess) return FO_ERR_HIP;
+    if ((int64_t)per_cu * pl->num_cus < gp.W) return FO_ERR_UNSUPPORTED;
+    GemmParams arg = gp;
+    void *args[] = {&arg};
+    if (hipLaunchCooperativeKernel(fn, dim3(gp.W), dim3(kThreads), args, C::LDS, s) != hipSuccess) return FO_ERR_HIP;
+    return FO_OK;
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, SIGNAL, false>), dim3(gp.W), dim3(kThreads), C::LDS, s, gp);
+    return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
+  }
 }
 
-template <typename T, bool SIGNAL>
+template <typename T, bool SIGNAL, bool SERIAL>
 int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
-  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, SIGNAL>(gp, s);
-  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, SIGNAL>(gp, s);
-  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, SIGNAL>(gp, s);
+  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, SIGNAL, SERIAL>(p, gp, s);
   return FO_ERR_UNSUPPORTED;
 }
 
 }  // namespace
 
 int launch_gemm(const fo_plan *p, const void *A, const void *B, void *Cout, bool rowmajor, uint32_t *sig,
-                uint32_t epoch, uint64_t *trace, hipStream_t s) {
+                uint32_t epoch, uint64_t *trace, uint32_t *serial, hipStream_t s) {
   if (p->NT == 0) return FO_OK;
   GemmParams gp{};
   gp.A = static_cast<const uint16_t *>(A);
@@ -430,9 +502,15 @@ int launch_gemm(const fo_plan *p, const void *A, const void *B, void *Cout, bool
   gp.trace = sig ? trace : nullptr;
   gp.epoch = epoch;
   gp.P = p->P;
-  const bool sig_on = gp.cnt != nullptr;
-  if (p->dtype == FO_BF16) return sig_on ? launch_tile<__bf16, true>(p, gp, s) : launch_tile<__bf16, false>(p, gp, s);
-  return sig_on ? launch_tile<_Float16, true>(p, gp, s) : launch_tile<_Float16, false>(p, gp, s);
+  gp.serial = serial;
+  gp.timeout_ticks = 2000000ull * p->ticks_per_us;  // 2 s per barrier wait
+  const bool bf = p->dtype == FO_BF16;
+  if (serial) {
+    if (!gp.cnt) return FO_ERR_INVALID;
+    return bf ? launch_tile<__bf16, true, true>(p, gp, s) : launch_tile<_Float16, true, true>(p, gp, s);
+  }
+  if (gp.cnt) return bf ? launch_tile<__bf16, true, false>(p, gp, s) : launch_tile<_Float16, true, false>(p, gp, s);
+  return bf ? launch_tile<__bf16, false, false>(p, gp, s) : launch_tile<_Float16, false, false>(p, gp, s);
 }
 
 }  // namespace fo

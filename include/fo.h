@@ -211,6 +211,23 @@ int fo_gemm_signal(const fo_plan *plan, const void *A, const void *B, void *reor
                    uint32_t *sig, uint32_t epoch, uint64_t *trace, hipStream_t stream);
 
 /*
+ * Debug form of fo_gemm_signal that makes the waves physical, so that the
+ * counting table's trajectory (deep-dive 一 › 实现方法, the worked example's
+ * table after every wave) can be read back: after wave w every workgroup
+ * meets at a device-wide barrier, workgroup 0 copies the signal words into
+ * snapshots[w*2P ..]: cnt[P] then flag[P], and a second barrier releases
+ * wave w+1.  Same arguments and results as fo_gemm_signal otherwise.
+ * snapshots: device uint32[T*2P + 2], zeroed by the caller before each
+ *      launch; the last two words are the barrier's arrival counter and a
+ *      status word, which receives FO_ERR_TIMEOUT if any barrier wait exceeds
+ *      2 s (every workgroup then leaves).
+ * The launch is cooperative: FO_ERR_UNSUPPORTED if the device cannot hold
+ * all W workgroups at once.  For tests and traces, not for the hot path.
+ */
+int fo_gemm_signal_serialized(const fo_plan *plan, const void *A, const void *B, void *reorder_buf,
+                              uint32_t *sig, uint32_t epoch, uint32_t *snapshots, hipStream_t stream);
+
+/*
  * The same GEMM main loop with a plain row-major epilogue and no signaling:
  * C[M, N] row-major.  Reference for the interference check.
  */

@@ -249,6 +249,36 @@ def test_gemm_signal_tables_and_layout(entry):
     assert np.array_equal(to_host(back), to_host(C))
 
 
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_serialized_waves_reproduce_the_counting_trajectory(entry):
+    """With a device-wide barrier after every wave the GPU's counting table after each wave is the
+    oracle's trajectory (deep-dive 一 › 实现方法: the worked example's table after each wave), the
+    flags rise exactly at each group's last wave, and the output is the normal launch's, bit for bit."""
+    o, p = _plans(entry)
+    A, B, _ = _inputs(entry, seed=500)
+    snaps_want, fire = oracle.counting_trajectory(o)
+    dA, dB = to_dev(A), to_dev(_stack(B))
+    ref = empty16(o.M * o.N)
+    p.gemm_signal(dA, dB, ref, p.new_sig(), 1)
+    buf = empty16(o.M * o.N)
+    sig = p.new_sig()
+    for epoch in (1, 2):
+        say(f"serialized waves {entry[0]} T={p.T} P={p.P} epoch={epoch}")
+        snaps = torch.zeros(2 * p.T * p.P + 2, dtype=torch.int32, device="cuda")
+        p.gemm_signal_serialized(dA, dB, buf, sig, epoch, snaps)
+        torch.cuda.synchronize()
+        s = snaps.cpu().numpy().astype(np.int64)
+        assert s[-1] == 0, fo.status_string(int(s[-1]))
+        assert s[-2] == 2 * p.T * p.W                              # every workgroup at every barrier
+        for w in range(p.T):
+            cnt = s[2 * w * p.P:2 * w * p.P + p.P]
+            flg = s[2 * w * p.P + p.P:2 * (w + 1) * p.P]
+            base = [(epoch - 1) * g for g in o.group_tiles]
+            assert cnt.tolist() == [b + x for b, x in zip(base, snaps_want[w])], (w, cnt.tolist())
+            assert flg.tolist() == [epoch if fire[j] <= w else epoch - 1 for j in range(p.P)], (w, flg.tolist())
+    assert np.array_equal(to_host(buf), to_host(ref))
+
+
 def test_gemm_each_workgroup_runs_its_wave_slot():
     """With W = 4 on the tiny shape, workgroup g runs dispatch indices g, g+4, g+8, g+12."""
     entry = PLANS[0]
