@@ -247,31 +247,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
   int64_t *rowoff = reinterpret_cast<int64_t *>(smem + C::ROWOFF);
 
+  // The tile a workgroup works on and its buffer resources.  A tile's first
+  // two K-slices are issued as soon as the previous tile's staging area is
+  // free, before that tile's signal, so the signal's waits overlap them.
+  TileDesc t = p.slots[0];
+  __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, 0), rb = make_rsrc(p.B, 0);
+  auto load_tile = [&](int bb) {
+    t = p.slots[bb];
+    ra = make_rsrc(p.A + (int64_t)t.row0 * p.K, t.rows * row_bytes);
+    rb = make_rsrc(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K, t.cols * row_bytes);
+  };
+  // K-slice kt -> LDS stage kt % 3, as C::LOADS DMA instructions per thread;
+  // part p of 4 issues instructions [p * DPB, (p + 1) * DPB)
+  constexpr int DPB = C::LOADS / 4;
+  auto stage_dst = [&](int kt) { return smem + (kt % kStages) * C::STAGE + wave * 1024; };
+#define FO_DMA_PART(PART, KT)                                                                              \
+  dma_part<PART, DPB, C::A_PER_T, C::B_PER_T>(ra, rb, stage_dst(KT), s_bofs, g_base, g_step,              \
+                                              (uint32_t)(KT) * kRowBytes)
+  auto issue = [&](int kt) {
+    FO_DMA_PART(0, kt);
+    FO_DMA_PART(1, kt);
+    FO_DMA_PART(2, kt);
+    FO_DMA_PART(3, kt);
+  };
+  auto prologue = [&]() {  // slices 0 and 1 of the current tile
+    issue(0);
+    if (nk > 1) issue(1);
+  };
+  if (pos < p.NT) {
+    load_tile(pos);
+    prologue();
+  }
+
   const int iters = SERIAL ? (p.NT + p.W - 1) / p.W : 0;
   for (int b = pos, it = 0; SERIAL ? it < iters : b < p.NT; b += p.W, ++it) {
     if (SERIAL && b >= p.NT) {  // no tile in this (partial) wave: only the barriers
       if (!wave_snapshot(p, it)) return;
       continue;
     }
-    const TileDesc t = p.slots[b];
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)t.row0 * p.K, t.rows * row_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K,
-                                                t.cols * row_bytes);
-
-    // K-slice kt -> LDS stage kt % 3, as C::LOADS DMA instructions per thread;
-    // part p of 4 issues instructions [p * DPB, (p + 1) * DPB)
-    constexpr int DPB = C::LOADS / 4;
-    // parts of slice kt's loads (stage kt % 3)
-    auto stage_dst = [&](int kt) { return smem + (kt % kStages) * C::STAGE + wave * 1024; };
-#define FO_DMA_PART(PART, KT)                                                                              \
-  dma_part<PART, DPB, C::A_PER_T, C::B_PER_T>(ra, rb, stage_dst(KT), s_bofs, g_base, g_step,              \
-                                              (uint32_t)(KT) * kRowBytes)
-    auto issue = [&](int kt) {
-      FO_DMA_PART(0, kt);
-      FO_DMA_PART(1, kt);
-      FO_DMA_PART(2, kt);
-      FO_DMA_PART(3, kt);
-    };
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -326,10 +339,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
     // Stage s holds slice s from when it is loaded (during slice s-2) until
     // its last fragments are read (third k-step of slice s): three LDS stages.
-    // Slice kt+2's loads are spread over the four blocks of slice kt.
-    issue(0);
+    // Slice kt+2's loads are spread over the four blocks of slice kt.  Slices
+    // 0 and 1 were issued ahead (prologue); anything this wave issued before
+    // them (the previous tile's stores) is older, so the same count holds.
     if (nk > 1) {
-      issue(1);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
     } else {
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -391,7 +404,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     three_blocks(nk - 1);
     mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
-#undef FO_DMA_PART
     __syncthreads();  // all fragment reads done before the staging tile overwrites the ring
 
     // ---- epilogue: destination of every valid row, then the 16-bit tile through LDS
@@ -418,33 +430,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       }
     }
 
-    // ---- signal: counting table, then the group's flag.  Either way the
-    // tile's stores complete here, so the next tile's load counting starts clean.
-    if constexpr (!SIGNAL) __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    // ---- next tile: once every wave has read the staging tile and the row
+    // offsets, its first slices may overwrite them.
+    __syncthreads();
+    const int grp = t.group;
+    const bool more = b + p.W < p.NT;
+    if (more) {
+      load_tile(b + p.W);
+      prologue();
+    }
+
+    // ---- signal: counting table, then the group's flag.  Each wave waits
+    // until its own tile stores are complete (the loads just issued may stay
+    // in flight: they are younger); after the barrier one lane releases the
+    // whole workgroup's stores to device scope (a single L2 write-back per
+    // tile) before it counts the tile.
     if constexpr (SIGNAL) {
-      // Each wave waits until its own tile stores are complete; after the
-      // barrier one lane releases the whole workgroup's stores to device scope
-      // (a single L2 write-back per tile) before it counts the tile.
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      if (!more)
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      else if (nk > 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::LOADS));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
       __syncthreads();
       if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t old = __hip_atomic_fetch_add(&p.cnt[t.group], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool fire = old + 1u == p.epoch * (uint32_t)p.thr[t.group];
-        if (fire) __hip_atomic_store(&p.flag[t.group], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(&p.cnt[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool fire = old + 1u == p.epoch * (uint32_t)p.thr[grp];
+        if (fire) __hip_atomic_store(&p.flag[grp], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         if (p.trace) {
           p.trace[2 * (int64_t)b] = wall_clock64();
           p.trace[2 * (int64_t)b + 1] = ((uint64_t)(uint32_t)g << 32) | old;
-          if (fire) __hip_atomic_fetch_add(&p.trace[2 * (int64_t)p.NT + t.group], (uint64_t)1, __ATOMIC_RELAXED,
+          if (fire) __hip_atomic_fetch_add(&p.trace[2 * (int64_t)p.NT + grp], (uint64_t)1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
-    __syncthreads();  // the next tile's first stage overwrites the staging area
     if constexpr (SERIAL) {
       if (!wave_snapshot(p, it)) return;
     }
   }
+#undef FO_DMA_PART
 }
 
 template <typename T, int BM, int BN, bool SIGNAL, bool SERIAL>
