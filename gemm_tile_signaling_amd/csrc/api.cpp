@@ -1,5 +1,6 @@
 // Enqueue calls of the C ABI: argument checks on the host, then the launchers.
-// Nothing here allocates, copies from the host or synchronises.
+// The enqueue calls allocate nothing, copy nothing from the host and never
+// synchronise; only fo_stream_create makes a runtime object (a stream).
 #include <cstdint>
 #include <vector>
 
@@ -16,6 +17,17 @@ bool device_ready(const fo_plan *p) { return p && !p->host_only && p->dev_block;
 // a buffer of M*N elements must be present and 16-byte aligned unless it is empty
 bool buf_ok(const fo_plan *p, const void *ptr) { return (p->M * p->N == 0) || (ptr && aligned16(ptr)); }
 
+// operands, reorder buffer, signal words and epoch of a signaling launch on a
+// non-empty plan; the counters reach epoch * |G_j|, which must fit in 32 bits
+bool signal_args_ok(const fo_plan *p, const void *A, const void *B, const void *reorder_buf, const uint32_t *sig,
+                    uint32_t epoch) {
+  if (!A || !B || !aligned16(A) || !aligned16(B) || !buf_ok(p, reorder_buf)) return false;
+  if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return false;
+  int32_t max_g = 0;
+  for (int32_t v : p->group_tiles) max_g = v > max_g ? v : max_g;
+  return (uint64_t)epoch * (uint64_t)max_g <= 0xFFFFFFFFull;
+}
+
 }  // namespace
 
 extern "C" {
@@ -24,12 +36,8 @@ int fo_gemm_signal(const fo_plan *p, const void *A, const void *B, void *reorder
                    uint64_t *trace, hipStream_t stream) {
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (p->NT == 0) return FO_OK;
-  if (!A || !B || !aligned16(A) || !aligned16(B) || !buf_ok(p, reorder_buf)) return FO_ERR_INVALID;
-  if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return FO_ERR_INVALID;
+  if (!signal_args_ok(p, A, B, reorder_buf, sig, epoch)) return FO_ERR_INVALID;
   if (trace && (reinterpret_cast<uintptr_t>(trace) & 7u)) return FO_ERR_INVALID;
-  int32_t max_g = 0;
-  for (int32_t v : p->group_tiles) max_g = v > max_g ? v : max_g;
-  if ((uint64_t)epoch * (uint64_t)max_g > 0xFFFFFFFFull) return FO_ERR_INVALID;
   return fo::launch_gemm(p, A, B, reorder_buf, false, sig, epoch, trace, nullptr, stream);
 }
 
@@ -37,12 +45,8 @@ int fo_gemm_signal_serialized(const fo_plan *p, const void *A, const void *B, vo
                               uint32_t epoch, uint32_t *snapshots, hipStream_t stream) {
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (p->NT == 0) return FO_OK;
-  if (!A || !B || !aligned16(A) || !aligned16(B) || !buf_ok(p, reorder_buf)) return FO_ERR_INVALID;
-  if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return FO_ERR_INVALID;
+  if (!signal_args_ok(p, A, B, reorder_buf, sig, epoch)) return FO_ERR_INVALID;
   if (!snapshots || (reinterpret_cast<uintptr_t>(snapshots) & 3u)) return FO_ERR_INVALID;
-  int32_t max_g = 0;
-  for (int32_t v : p->group_tiles) max_g = v > max_g ? v : max_g;
-  if ((uint64_t)epoch * (uint64_t)max_g > 0xFFFFFFFFull) return FO_ERR_INVALID;
   return fo::launch_gemm(p, A, B, reorder_buf, false, sig, epoch, nullptr, snapshots, stream);
 }
 

@@ -10,9 +10,11 @@
 //   * persistent grid of exactly W workgroups (W = wave size); workgroup g
 //     runs dispatch indices pos(g), pos(g) + W, ... so wave w is every
 //     workgroup's w-th tile.  pos() packs each XCD's workgroups (hardware
-//     places workgroup g on XCD g % 8) onto a contiguous run of positions of
-//     the wave, so the tiles sharing an XCD's L2 are neighbours in the
-//     swizzled order.  This only permutes workgroups inside a wave.
+//     deals consecutive workgroups round-robin over the 8 XCDs, so the
+//     workgroups with one value of g % 8 share an XCD) onto a contiguous run
+//     of positions of the wave, so the tiles sharing an XCD's L2 are
+//     neighbours in the swizzled order.  This only permutes workgroups
+//     inside a wave.
 //   * 256 threads = 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2)
 //     sub-tile made of 32 x 32 blocks computed with v_mfma_f32_32x32x16.
 //     A and B fragments are passed to the MFMA swapped (B as the first
@@ -43,11 +45,17 @@
 //     never touch memory outside the problem.
 //   * Epilogue: accumulators -> 16-bit -> LDS staging tile; every valid row's
 //     destination offset (row-major, banded or subtoken layout) is computed
-//     once into LDS; then 16-byte coalesced stores.  With signaling on, each
-//     wave waits for its stores to complete, the workgroup meets at a
-//     barrier, and one lane releases the tile to device scope and increments
-//     cnt[group]; the lane that brings it to epoch * |G_group| stores
-//     flag[group] = epoch with release semantics.
+//     once into LDS; then 16-byte coalesced stores.  Once every wave has read
+//     the staging tile, the workgroup issues the next tile's first two
+//     K-slices.  With signaling on, each wave then waits for its own stores
+//     to complete (the younger loads stay in flight), the workgroup meets at
+//     a barrier, and one lane releases the tile to device scope and
+//     increments cnt[group]; the lane that brings it to epoch * |G_group|
+//     stores flag[group] = epoch with release semantics.  The signal's waits
+//     thus overlap the next tile's first loads.
+//   * A third instantiation serializes the waves for tests and traces (a
+//     device-wide barrier and a snapshot of the signal words after every
+//     wave, cooperative launch); the hot path never runs it.
 #include "../fo_internal.h"
 #include "buffer.h"
 

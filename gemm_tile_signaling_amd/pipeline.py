@@ -1,15 +1,21 @@
 """One pass of the hot path on two HIP streams, built from the C-ABI calls.
 
-Stream A runs the signaling GEMM; stream B runs the consumer and then the
-post-communication reorder.  The two streams are linked on the device only
-through the signal words (counting table + flags); the host orders only
-consecutive passes (the next GEMM reuses the reordered buffer, so stream A
-waits for the previous pass's reorder to finish).
+One stream runs the signaling GEMM; the other runs the consumer and then the
+post-communication reorder.  The two are linked on the device only through
+the signal words (counting table + flags).  Passes are kept in order: a
+pass's GEMM starts after the previous pass's post-reorder, as a layer's GEMM
+waits for the previous layer's output.  The two streams swap roles every
+pass, so that ordering is the hardware queue's own (the GEMM is queued
+behind the previous post-reorder on the same stream) instead of a
+cross-queue event on the critical path; the only cross-stream wait, the
+consumer's on the previous post-reorder (it rewrites recv), runs while the
+GEMM computes.
 
 Streams: both come from ``fo_stream_create``, so each has a hardware queue of
 its own and the consumer really runs beside the GEMM.  Launch order: the GEMM
-is enqueued before the consumer; the GEMM never waits for anything, so even
-streams that shared a queue would complete (serialised, without overlap).
+is enqueued before its consumer and waits only for earlier passes' kernels,
+none of which wait for it, so even streams that shared a queue would
+complete (serialised, without overlap).
 
 Buffers (torch tensors, 16-bit elements stored as int16):
   A [M*K], B [problems*N*K], reorder_buf / peer / recv / out [M*N],
@@ -42,7 +48,7 @@ class Pipeline:
         with torch.cuda.device(dev):
             self.sa = stream_create()
             self.sb = stream_create()
-        self.done_b = torch.cuda.Event()
+        self.done_post = torch.cuda.Event()
         self.epoch = 0
         self.consumer_workgroups = consumer_workgroups
         self.timeout_us = timeout_us
@@ -51,7 +57,7 @@ class Pipeline:
         ready.record(torch.cuda.current_stream(dev))
         self.sa.wait_event(ready)
         self.sb.wait_event(ready)
-        self.done_b.record(self.sb)
+        self.done_post.record(self.sb)
 
     def close(self):
         """Wait for the streams, then release them."""
@@ -75,23 +81,25 @@ class Pipeline:
         p = self.plan
         self.epoch += 1
         e = self.epoch
-        self.sa.wait_event(self.done_b)
+        # the previous pass's consumer and post-reorder ran on s_gemm: the GEMM queues behind them
+        s_gemm, s_comm = (self.sa, self.sb) if e % 2 == 0 else (self.sb, self.sa)
+        s_comm.wait_event(self.done_post)
         if events:
-            events["gemm"][0].record(self.sa)
-        p.gemm_signal(self.A, self.B, self.buf, self.sig, e, trace=trace, stream=self.sa)
+            events["gemm"][0].record(s_gemm)
+        p.gemm_signal(self.A, self.B, self.buf, self.sig, e, trace=trace, stream=s_gemm)
         if events:
-            events["gemm"][1].record(self.sa)
-            events["consume"][0].record(self.sb)
+            events["gemm"][1].record(s_gemm)
+            events["consume"][0].record(s_comm)
         p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status,
                         timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
-                        trace=consumer_trace, stream=self.sb)
+                        trace=consumer_trace, stream=s_comm)
         if events:
-            events["consume"][1].record(self.sb)
-            events["post"][0].record(self.sb)
-        p.reorder_post(self.recv, self.out, stream=self.sb)
+            events["consume"][1].record(s_comm)
+            events["post"][0].record(s_comm)
+        p.reorder_post(self.recv, self.out, stream=s_comm)
         if events:
-            events["post"][1].record(self.sb)
-        self.done_b.record(self.sb)
+            events["post"][1].record(s_comm)
+        self.done_post.record(s_comm)
         return e
 
     def join(self):
