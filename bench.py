@@ -41,6 +41,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="profiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (prefill, decode, ReduceScatter, MoE All-to-All)")
     ap.add_argument("--no-search", action="store_true",
                     help="skip the check of the predictive partition search against measured partitions")
     ap.add_argument("--counters", action="store_true",
@@ -79,6 +81,72 @@ def wave_pattern_of(t_sig, W, tick_us, bins=40):
     return {"waves": per,
             "gap_us": [round(per[i + 1]["first_us"] - per[i]["last_us"], 2) for i in range(T - 1)],
             "bin_us": round(float(edges[1] - edges[0]), 3), "histogram": hist}
+
+
+def configs_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
+    """The other workloads beside the headline: signaling and plain GEMM alone, and one pass of the
+    pipeline at each workload's first partition (one wave per group if it names none).
+
+    Inputs are drawn on the device from the workload's distribution (the parity tests use the seeded host
+    inputs; throughput does not depend on the exact values).  MoE: useful FLOP count the routed rows only.
+    """
+    from workloads import WORKLOADS, moe_routing
+    out = []
+    s = torch.cuda.Stream(device=dev)
+    td = {"bf16": torch.bfloat16, "fp16": torch.float16}
+    for name in ("ar_prefill", "ar_decode", "rs", "moe_a2a"):
+        w = WORKLOADS[name]
+        if w.experts:
+            m_per, tok = moe_routing(w)
+            row_dest = tok // (w.tokens // w.ranks)
+        else:
+            m_per, row_dest = [w.M], None
+        M = sum(m_per)
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed_base)
+        std = w.dist[1] if w.dist[0] == "normal" else 1.0
+        dA = (torch.randn(M * w.K, device=dev, generator=g) * std).to(td[w.dtype]).view(torch.int16)
+        dB = (torch.randn(len(m_per) * w.N * w.K, device=dev, generator=g) * std).to(td[w.dtype]).view(torch.int16)
+        dpeer = (torch.randn(M * w.N, device=dev, generator=g) * std).to(td[w.dtype]).view(torch.int16)
+        comp = w.compositions[0] if w.compositions else None
+        plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp,
+                       mode=w.mode, ranks=w.ranks, row_dest=row_dest)
+        flops = 2.0 * M * w.N * w.K
+        C = torch.empty(M * w.N, dtype=torch.int16, device=dev)
+        sig = plan.new_sig(dev)
+        ep = [0]
+
+        def _sig(st):
+            ep[0] += 1
+            plan.gemm_signal(dA, dB, C, sig, ep[0], stream=st)
+        for _ in range(3):
+            _sig(s)
+        sig_ms = _time_kernel(torch, _sig, s, 10)
+        plain_ms = _time_kernel(torch, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, 10)
+        pipe = Pipeline(plan, dA, dB, dpeer)
+        for _ in range(warmup):
+            pipe.step()
+        pipe.join()
+        torch.cuda.synchronize()
+        evs = [{k: _event_pairs(torch, 1)[0] for k in ("gemm", "consume", "post")} for _ in range(steps)]
+        for e in evs:
+            pipe.step(events=e)
+        pipe.join()
+        torch.cuda.synchronize()
+        if int(pipe.status.item()) != 0:
+            raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
+        gemm_pipe_ms = float(np.median([e["gemm"][0].elapsed_time(e["gemm"][1]) for e in evs]))
+        pass_ms = float(np.median([e["gemm"][0].elapsed_time(e["post"][1]) for e in evs]))
+        pipe.close()
+        out.append({"workload": f"{name}: M={M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, {plan.NT} tiles, T={plan.T}, "
+                                f"mode {w.mode}, groups {list(comp) if comp else [1] * plan.T}",
+                    "signal_gemm_alone_tflops": round(flops / (sig_ms * 1e-3) / 1e12, 1),
+                    "plain_gemm_alone_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 1),
+                    "signal_gemm_in_pass_tflops": round(flops / (gemm_pipe_ms * 1e-3) / 1e12, 1),
+                    "frac_of_peak": round(flops / (gemm_pipe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "pass_ms": round(pass_ms, 4)})
+        del dA, dB, dpeer, C
+    return out
 
 
 def search_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
@@ -291,18 +359,27 @@ def main():
             pipe.step()
         pipe.join()
         torch.cuda.synchronize()
-        evs = {k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")}
+        # timed: K passes; only the GEMM is bracketed by events (on its own stream), since every event
+        # is a packet in a hardware queue and adds to the pass
+        gemm_ev = _event_pairs(torch, a.steps)
         t0 = time.perf_counter()
         for i in range(a.steps):
-            pipe.step(events={k: v[i] for k, v in evs.items()})
+            pipe.step(events={"gemm": gemm_ev[i]})
         pipe.join()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         if int(pipe.status.item()) != 0:
             raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
+        gemm_ms = float(np.mean([s.elapsed_time(e) for s, e in gemm_ev]))
+        # untimed: the same number of passes with every kernel bracketed, for the breakdown
+        evs = {k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")}
+        for i in range(a.steps):
+            pipe.step(events={k: v[i] for k, v in evs.items()})
+        pipe.join()
+        torch.cuda.synchronize()
         avg = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in evs.items()}
         results.append(dict(plan=plan, pipe=pipe, comp=comp or tuple([1] * plan.T), step_ms=el * 1e3 / a.steps,
-                            gemm_ms=avg["gemm"], consume_ms=avg["consume"], post_ms=avg["post"]))
+                            gemm_ms=gemm_ms, consume_ms=avg["consume"], post_ms=avg["post"]))
     best = min(results, key=lambda r: r["step_ms"])
     plan, pipe = best["plan"], best["pipe"]
 
@@ -386,6 +463,8 @@ def main():
                         "post_ms": round(r["post_ms"], 4)} for r in results],
         "cpu_baseline": None,
     }
+    if not a.no_configs:
+        line["configs"] = configs_check(torch, fo, Pipeline, dev)
     if not a.no_search:
         line["search"] = search_check(torch, fo, Pipeline, dev)
     if not a.no_cpu_baseline:

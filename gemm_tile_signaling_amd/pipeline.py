@@ -76,29 +76,32 @@ class Pipeline:
 
     def step(self, trace=None, consumer_trace=None, events: Optional[dict] = None):
         """Enqueue one pass; returns the epoch it used.  ``events`` may hold
-        torch.cuda.Event pairs recorded around each kernel on its own stream:
-        keys 'gemm', 'consume', 'post' -> (start, end)."""
+        torch.cuda.Event pairs recorded around a kernel on its own stream, under
+        any of the keys 'gemm', 'consume', 'post' -> (start, end)."""
         p = self.plan
         self.epoch += 1
         e = self.epoch
         # the previous pass's consumer and post-reorder ran on s_gemm: the GEMM queues behind them
         s_gemm, s_comm = (self.sa, self.sb) if e % 2 == 0 else (self.sb, self.sa)
         s_comm.wait_event(self.done_post)
-        if events:
-            events["gemm"][0].record(s_gemm)
+        ev = events or {}
+        if "gemm" in ev:
+            ev["gemm"][0].record(s_gemm)
         p.gemm_signal(self.A, self.B, self.buf, self.sig, e, trace=trace, stream=s_gemm)
-        if events:
-            events["gemm"][1].record(s_gemm)
-            events["consume"][0].record(s_comm)
+        if "gemm" in ev:
+            ev["gemm"][1].record(s_gemm)
+        if "consume" in ev:
+            ev["consume"][0].record(s_comm)
         p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status,
                         timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
                         trace=consumer_trace, stream=s_comm)
-        if events:
-            events["consume"][1].record(s_comm)
-            events["post"][0].record(s_comm)
+        if "consume" in ev:
+            ev["consume"][1].record(s_comm)
+        if "post" in ev:
+            ev["post"][0].record(s_comm)
         p.reorder_post(self.recv, self.out, stream=s_comm)
-        if events:
-            events["post"][1].record(s_comm)
+        if "post" in ev:
+            ev["post"][1].record(s_comm)
         self.done_post.record(s_comm)
         return e
 
