@@ -370,7 +370,8 @@ def main():
         el = time.perf_counter() - t0
         if int(pipe.status.item()) != 0:
             raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
-        gemm_ms = float(np.mean([s.elapsed_time(e) for s, e in gemm_ev]))
+        gemm_each = [s.elapsed_time(e) for s, e in gemm_ev]
+        gemm_ms = float(np.mean(gemm_each))
         # untimed: the same number of passes with every kernel bracketed, for the breakdown
         evs = {k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")}
         for i in range(a.steps):
@@ -379,9 +380,24 @@ def main():
         torch.cuda.synchronize()
         avg = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in evs.items()}
         results.append(dict(plan=plan, pipe=pipe, comp=comp or tuple([1] * plan.T), step_ms=el * 1e3 / a.steps,
-                            gemm_ms=gemm_ms, consume_ms=avg["consume"], post_ms=avg["post"]))
+                            gemm_ms=gemm_ms, gemm_q=np.percentile(gemm_each, [10, 50, 90]).tolist(),
+                            consume_ms=avg["consume"], post_ms=avg["post"]))
     best = min(results, key=lambda r: r["step_ms"])
     plan, pipe = best["plan"], best["pipe"]
+
+    # the same passes without overlap (GEMM, then consumer, then post-reorder on one queue), timed the same way
+    for _ in range(a.warmup):
+        pipe.step(serial=True)
+    pipe.join()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        pipe.step(serial=True)
+    pipe.join()
+    torch.cuda.synchronize()
+    serial_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    if int(pipe.status.item()) != 0:
+        raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
 
     # one traced pass: device wall-clock stamps of every tile's signal and of each consumer wait
     gtr = torch.zeros(2 * plan.NT + plan.P, dtype=torch.int64, device=dev)
@@ -422,6 +438,19 @@ def main():
                                                                         else torch.float16).view(torch.int16)
     post_ep_ms = _time_kernel(torch, lambda st: plan.reorder_post_ep(recv, C, bias=bias, act="silu", stream=st), s,
                               n_alone, scratch)
+    # context only: the library GEMM (hipBLASLt through torch) on the same operands, C = A . B^T
+    a_mat = dA.view(torch.bfloat16 if w.dtype == "bf16" else torch.float16).view(w.M, w.K)
+    b_mat = dB.view(a_mat.dtype).view(w.N, w.K)
+    c_mat = torch.empty(w.M, w.N, dtype=a_mat.dtype, device=dev)
+
+    def _lib(st):
+        with torch.cuda.stream(st):
+            torch.mm(a_mat, b_mat.t(), out=c_mat)
+    for _ in range(3):
+        _lib(s)
+    torch.cuda.synchronize()
+    lib_ms = _time_kernel(torch, _lib, s, n_alone)
+    del c_mat
     mn = w.M * w.N
     consume_gbps = 6.0 * mn / (consume_ms * 1e-3) / 1e9
     post_gbps = 4.0 * mn / (post_ms * 1e-3) / 1e9
@@ -445,10 +474,14 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes": 2 * (w.M * w.K + w.N * w.K + w.M * w.N),
                      "kernel": "signaling GEMM (stream A, consumer resident)"},
+        "signal_gemm_us_p10_p50_p90": [round(x * 1e3, 1) for x in best["gemm_q"]],
+        "serial_pass_ms": round(serial_ms, 4),
+        "overlap_speedup_over_serial": round(serial_ms / best["step_ms"], 4),
         "signal_gemm_alone_tflops": round(flops / (signal_ms * 1e-3) / 1e12, 2),
         "plain_gemm_alone_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
         "signal_over_plain_alone": round(plain_ms / signal_ms, 4),
         "signal_with_consumer_over_plain": round(plain_ms / best["gemm_ms"], 4),
+        "context_library_gemm_tflops": round(flops / (lib_ms * 1e-3) / 1e12, 2),
         "consumer_alone_gbps": round(consume_gbps, 1),
         "post_reorder_alone_gbps": round(post_gbps, 1),
         "post_reorder_bias_silu_alone_gbps": round((4.0 * mn + 2.0 * plan.num_problems * w.N) / (post_ep_ms * 1e-3) / 1e9,

@@ -6,10 +6,11 @@ the signal words (counting table + flags).  Passes are kept in order: a
 pass's GEMM starts after the previous pass's post-reorder, as a layer's GEMM
 waits for the previous layer's output.  The two streams swap roles every
 pass, so that ordering is the hardware queue's own (the GEMM is queued
-behind the previous post-reorder on the same stream) instead of a
-cross-queue event on the critical path; the only cross-stream wait, the
-consumer's on the previous post-reorder (it rewrites recv), runs while the
-GEMM computes.
+behind the previous post-reorder on the same stream) and no event sits on
+the critical path.  The consumer needs no event either: it may start as soon
+as the previous GEMM on its queue ends, but it touches its buffers only once
+a flag of its own epoch is raised, i.e. after this pass's GEMM has started,
+which is after the previous post-reorder (the last reader of recv) ended.
 
 Streams: both come from ``fo_stream_create``, so each has a hardware queue of
 its own and the consumer really runs beside the GEMM.  Launch order: the GEMM
@@ -48,7 +49,6 @@ class Pipeline:
         with torch.cuda.device(dev):
             self.sa = stream_create()
             self.sb = stream_create()
-        self.done_post = torch.cuda.Event()
         self.epoch = 0
         self.consumer_workgroups = consumer_workgroups
         self.timeout_us = timeout_us
@@ -57,7 +57,7 @@ class Pipeline:
         ready.record(torch.cuda.current_stream(dev))
         self.sa.wait_event(ready)
         self.sb.wait_event(ready)
-        self.done_post.record(self.sb)
+        self.post_stream = self.sb   # the queue the last post-reorder was enqueued on
 
     def close(self):
         """Wait for the streams, then release them."""
@@ -74,16 +74,27 @@ class Pipeline:
         except Exception:
             pass
 
-    def step(self, trace=None, consumer_trace=None, events: Optional[dict] = None):
+    def step(self, trace=None, consumer_trace=None, events: Optional[dict] = None, serial: bool = False):
         """Enqueue one pass; returns the epoch it used.  ``events`` may hold
         torch.cuda.Event pairs recorded around a kernel on its own stream, under
-        any of the keys 'gemm', 'consume', 'post' -> (start, end)."""
+        any of the keys 'gemm', 'consume', 'post' -> (start, end).  ``serial``
+        puts the three kernels on one queue, so the consumer starts only after
+        the GEMM has finished (every flag already raised): the same pass without
+        overlap, for comparison."""
         p = self.plan
         self.epoch += 1
         e = self.epoch
         # the previous pass's consumer and post-reorder ran on s_gemm: the GEMM queues behind them
-        s_gemm, s_comm = (self.sa, self.sb) if e % 2 == 0 else (self.sb, self.sa)
-        s_comm.wait_event(self.done_post)
+        if serial:
+            s_gemm = s_comm = self.sa
+        else:
+            s_gemm, s_comm = (self.sa, self.sb) if e % 2 == 0 else (self.sb, self.sa)
+        if s_gemm is not self.post_stream:
+            # only next to a pass without overlap: order this GEMM after the previous post-reorder
+            # (two GEMMs in flight at once would interleave their epochs' counts)
+            done = self.torch.cuda.Event()
+            done.record(self.post_stream)
+            s_gemm.wait_event(done)
         ev = events or {}
         if "gemm" in ev:
             ev["gemm"][0].record(s_gemm)
@@ -102,7 +113,7 @@ class Pipeline:
         p.reorder_post(self.recv, self.out, stream=s_comm)
         if "post" in ev:
             ev["post"][1].record(s_comm)
-        self.done_post.record(s_comm)
+        self.post_stream = s_comm
         return e
 
     def join(self):

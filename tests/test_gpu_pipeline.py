@@ -81,3 +81,25 @@ def test_tiny_workload_every_partition_kind(comp):
     want = oracle.round_to_dtype(oracle.decode_bits(r["C"], w.dtype) + oracle.decode_bits(peer, w.dtype)[r["off"]],
                                  w.dtype)
     tol_check_out(to_host(pipe.out).reshape(o.M, o.N), want, r["C64"], w.dtype, "out")
+
+
+@pytest.mark.parametrize("entry", [e for e in PLANS if e[3] <= 256], ids=[e[0] for e in PLANS if e[3] <= 256])
+def test_serial_passes_between_overlapped_ones(entry):
+    """Passes without overlap (all three kernels on one queue) interleaved with
+    overlapped ones: every pass is bit-exact against the oracle and the counting
+    table keeps counting epochs."""
+    o, p = _plans(entry)
+    dt = entry[4]
+    A, B, peer = _inputs(entry, dist=("ternary",), seed=610)
+    r = oracle.run_pipeline(A, B, peer, o, dt)
+    say(f"pipeline serial/overlapped {entry[0]}")
+    pipe = Pipeline(p, to_dev(A), to_dev(_stack(B)), to_dev(peer))
+    for serial in (True, False, True, True, False):
+        pipe.step(serial=serial)
+    pipe.join()
+    torch.cuda.synchronize()
+    assert int(pipe.status.item()) == 0
+    s = pipe.sig.cpu().numpy()
+    assert s[:p.P].tolist() == [5 * g for g in o.group_tiles]
+    assert s[p.flag_offset:p.flag_offset + p.P].tolist() == [5] * p.P
+    assert np.array_equal(to_host(pipe.out), r["out"].ravel())
