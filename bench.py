@@ -350,54 +350,70 @@ def main():
                           "calibration_copy_bytes": 256 * 2 ** 20, "status": int(status.item())}), flush=True)
         return
 
-    results = []
+    pipes = []
     for comp in comps:
         plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W,
                        composition=comp, mode=w.mode, ranks=w.ranks, row_dest=row_dest)
-        pipe = Pipeline(plan, dA, dB, dpeer)
-        for _ in range(a.warmup):
-            pipe.step()
+        pipes.append(dict(plan=plan, pipe=Pipeline(plan, dA, dB, dpeer), comp=comp or tuple([1] * plan.T)))
+    launches = [0]   # signaling-GEMM launches so far (locates the timed region in a kernel trace)
+
+    def passes(pipe, n, **kw):
+        for _ in range(n):
+            pipe.step(**kw)
+        launches[0] += n
         pipe.join()
         torch.cuda.synchronize()
-        # timed: K passes; only the GEMM is bracketed by events (on its own stream), since every event
-        # is a packet in a hardware queue and adds to the pass
-        gemm_ev = _event_pairs(torch, a.steps)
-        t0 = time.perf_counter()
-        for i in range(a.steps):
-            pipe.step(events={"gemm": gemm_ev[i]})
-        pipe.join()
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
         if int(pipe.status.item()) != 0:
             raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
-        gemm_each = [s.elapsed_time(e) for s, e in gemm_ev]
-        gemm_ms = float(np.mean(gemm_each))
-        # untimed: the same number of passes with every kernel bracketed, for the breakdown
-        evs = {k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")}
-        for i in range(a.steps):
-            pipe.step(events={k: v[i] for k, v in evs.items()})
-        pipe.join()
-        torch.cuda.synchronize()
-        avg = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in evs.items()}
-        results.append(dict(plan=plan, pipe=pipe, comp=comp or tuple([1] * plan.T), step_ms=el * 1e3 / a.steps,
-                            gemm_ms=gemm_ms, gemm_q=np.percentile(gemm_each, [10, 50, 90]).tolist(),
-                            consume_ms=avg["consume"], post_ms=avg["post"]))
-    best = min(results, key=lambda r: r["step_ms"])
+
+    # choose the partition: short blocks of passes, every schedule in turn, three rounds, so that
+    # clock and power drift falls on all of them alike; the serial schedule (GEMM, then consumer,
+    # then post-reorder, one queue) is measured the same way for comparison
+    passes(pipes[0]["pipe"], a.warmup)
+    n_pick = max(10, a.steps // 2)
+    sched = [(i, False) for i in range(len(pipes))] + [(0, True)]
+    picks = {k: [] for k in sched}
+    for _ in range(3):
+        for i, serial in sched:
+            passes(pipes[i]["pipe"], 5, serial=serial)
+            t0 = time.perf_counter()
+            passes(pipes[i]["pipe"], n_pick, serial=serial)
+            picks[(i, serial)].append((time.perf_counter() - t0) * 1e3 / n_pick)
+    for i, r in enumerate(pipes):
+        r["pick_ms"] = float(np.median(picks[(i, False)]))
+    serial_ms = float(np.median(picks[(0, True)]))
+    best = min(pipes, key=lambda r: r["pick_ms"])
     plan, pipe = best["plan"], best["pipe"]
 
-    # the same passes without overlap (GEMM, then consumer, then post-reorder on one queue), timed the same way
-    for _ in range(a.warmup):
-        pipe.step(serial=True)
-    pipe.join()
-    torch.cuda.synchronize()
+    # timed: W warm-up passes, then K passes of the chosen partition; only the GEMM is bracketed by
+    # events (on its own stream), since every event is a packet in a hardware queue and adds to the pass
+    passes(pipe, a.warmup)
+    timed_first = launches[0]
+    gemm_ev = _event_pairs(torch, a.steps)
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        pipe.step(serial=True)
+    for i in range(a.steps):
+        pipe.step(events={"gemm": gemm_ev[i]})
+    launches[0] += a.steps
     pipe.join()
     torch.cuda.synchronize()
-    serial_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    el = time.perf_counter() - t0
     if int(pipe.status.item()) != 0:
         raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
+    gemm_each = [s.elapsed_time(e) for s, e in gemm_ev]
+    best.update(step_ms=el * 1e3 / a.steps, gemm_ms=float(np.mean(gemm_each)),
+                gemm_q=np.percentile(gemm_each, [10, 50, 90]).tolist())
+    timed_range = [timed_first, launches[0]]
+
+    # untimed: every kernel of every partition bracketed, for the breakdown
+    for r in pipes:
+        evs = {k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")}
+        for i in range(a.steps):
+            r["pipe"].step(events={k: v[i] for k, v in evs.items()})
+        launches[0] += a.steps
+        r["pipe"].join()
+        torch.cuda.synchronize()
+        avg = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in evs.items()}
+        r.update(br_gemm_ms=avg["gemm"], consume_ms=avg["consume"], post_ms=avg["post"])
 
     # one traced pass: device wall-clock stamps of every tile's signal and of each consumer wait
     gtr = torch.zeros(2 * plan.NT + plan.P, dtype=torch.int64, device=dev)
@@ -476,7 +492,7 @@ def main():
                      "kernel": "signaling GEMM (stream A, consumer resident)"},
         "signal_gemm_us_p10_p50_p90": [round(x * 1e3, 1) for x in best["gemm_q"]],
         "serial_pass_ms": round(serial_ms, 4),
-        "overlap_speedup_over_serial": round(serial_ms / best["step_ms"], 4),
+        "overlap_speedup_over_serial": round(serial_ms / best["pick_ms"], 4),
         "signal_gemm_alone_tflops": round(flops / (signal_ms * 1e-3) / 1e12, 2),
         "plain_gemm_alone_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
         "signal_over_plain_alone": round(plain_ms / signal_ms, 4),
@@ -491,9 +507,10 @@ def main():
         "signal_to_consume_us": signal_to_consume_us,
         "first_group_consumed_before_gemm_end_us": first_consume_before_gemm_end_us,
         "wave_pattern": wave_pattern,
-        "partitions": [{"groups": list(r["comp"]), "step_ms": round(r["step_ms"], 4),
-                        "gemm_ms": round(r["gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
-                        "post_ms": round(r["post_ms"], 4)} for r in results],
+        "partitions": [{"groups": list(r["comp"]), "pick_step_ms": round(r["pick_ms"], 4),
+                        "gemm_ms": round(r["br_gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
+                        "post_ms": round(r["post_ms"], 4)} for r in pipes],
+        "timed_signal_gemm_launches": timed_range,
         "cpu_baseline": None,
     }
     if not a.no_configs:
