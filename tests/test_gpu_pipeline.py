@@ -103,3 +103,34 @@ def test_serial_passes_between_overlapped_ones(entry):
     assert s[:p.P].tolist() == [5 * g for g in o.group_tiles]
     assert s[p.flag_offset:p.flag_offset + p.P].tolist() == [5] * p.P
     assert np.array_equal(to_host(pipe.out), r["out"].ravel())
+
+
+@pytest.mark.parametrize("entry", [e for e in PLANS if e[0] in ("ragged_256", "subtile_r4", "tiny_fp16")],
+                         ids=lambda e: e[0])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_back_to_back_passes_keep_recv_ordered(entry, in_place):
+    """Consecutive passes alternate between two peer buffers and write separate
+    outputs, so a consumer that rewrote recv before the previous pass's
+    post-reorder had read it would leave the other peer's sums in an output.
+    Every output is checked bit-exactly (ternary inputs) against the oracle."""
+    o, p = _plans(entry)
+    dt = entry[4]
+    A, B, peer0 = _inputs(entry, dist=("ternary",), seed=620)
+    peer1 = _inputs(entry, dist=("ternary",), seed=640)[2]
+    want = [oracle.run_pipeline(A, B, pr, o, dt)["out"].ravel() for pr in (peer0, peer1)]
+    assert not np.array_equal(want[0], want[1])
+    n = 40
+    say(f"pipeline back-to-back {entry[0]}, {n} passes, in_place={in_place}")
+    peers = [to_dev(peer0), to_dev(peer1)]
+    pipe = Pipeline(p, to_dev(A), to_dev(_stack(B)), peers[0], in_place=in_place)
+    outs = [torch.empty(o.M * o.N, dtype=torch.int16, device="cuda") for _ in range(n)]
+    for i in range(n):
+        pipe.peer = peers[i % 2]
+        pipe.out = outs[i]
+        pipe.step()
+    pipe.join()
+    torch.cuda.synchronize()
+    assert int(pipe.status.item()) == 0
+    assert pipe.sig.cpu().numpy()[:p.P].tolist() == [n * g for g in o.group_tiles]
+    for i in range(n):
+        assert np.array_equal(to_host(outs[i]), want[i % 2]), f"pass {i}"
