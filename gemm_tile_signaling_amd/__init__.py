@@ -85,6 +85,7 @@ def lib() -> C.CDLL:
             "fo_stream_create": [C.POINTER(vp)],
             "fo_stream_destroy": [vp],
             "fo_reorder_post": [vp, vp, vp, vp],
+            "fo_reorder_post_groups": [vp, i32, i32, vp, vp, vp],
             "fo_reorder_pre": [vp, vp, vp, vp],
             "fo_reorder_post_ep": [vp, vp, vp, vp, i32, vp],
         }
@@ -286,10 +287,16 @@ class Plan:
             _ptr(status, numel=1, itemsize=4, name="status"), int(timeout_us), int(num_workgroups),
             _ptr(trace, numel=self.P, itemsize=8, name="trace"), _stream(stream)), "fo_consume_group")
 
-    def reorder_post(self, reordered, out, stream=None):
-        _check(lib().fo_reorder_post(self._h, _ptr(reordered, numel=self.mn, itemsize=2, name="reordered"),
-                                     _ptr(out, numel=self.mn, itemsize=2, name="out"), _stream(stream)),
-               "fo_reorder_post")
+    def reorder_post(self, reordered, out, stream=None, groups: Optional[tuple] = None):
+        """Inverse mapping into row-major ``out``; ``groups=(g_begin, g_end)`` restricts it to the
+        tiles of those groups (``fo_reorder_post_groups``)."""
+        src = _ptr(reordered, numel=self.mn, itemsize=2, name="reordered")
+        dst = _ptr(out, numel=self.mn, itemsize=2, name="out")
+        if groups is None:
+            _check(lib().fo_reorder_post(self._h, src, dst, _stream(stream)), "fo_reorder_post")
+        else:
+            _check(lib().fo_reorder_post_groups(self._h, int(groups[0]), int(groups[1]), src, dst, _stream(stream)),
+                   "fo_reorder_post_groups")
 
     def reorder_post_ep(self, reordered, out, bias=None, act: str = "none", stream=None):
         """Post-communication reorder fused with bias + activation (``fo_reorder_post_ep``)."""

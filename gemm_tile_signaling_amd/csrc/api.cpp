@@ -78,7 +78,20 @@ int fo_consume_group(const fo_plan *p, const void *send, const void *peer, void 
 int fo_reorder_post(const fo_plan *p, const void *reordered, void *out, hipStream_t stream) {
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (!buf_ok(p, reordered) || !buf_ok(p, out)) return FO_ERR_INVALID;
-  return fo::launch_reorder(p, reordered, out, true, stream);
+  return fo::launch_reorder(p, reordered, out, true, 0, p->NT, stream);
+}
+
+int fo_reorder_post_groups(const fo_plan *p, int32_t g_begin, int32_t g_end, const void *reordered, void *out,
+                           hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (g_begin < 0 || g_end > p->P || g_begin > g_end) return FO_ERR_INVALID;
+  if (!buf_ok(p, reordered) || !buf_ok(p, out)) return FO_ERR_INVALID;
+  int32_t first = 0, last = 0;  // slots of groups [g_begin, g_end): consecutive, in group order
+  for (int32_t g = 0; g < g_end; ++g) {
+    if (g < g_begin) first += p->group_tiles[g];
+    last += p->group_tiles[g];
+  }
+  return fo::launch_reorder(p, reordered, out, true, first, last, stream);
 }
 
 int fo_reorder_post_ep(const fo_plan *p, const void *reordered, void *out, const void *bias, int32_t act,
@@ -93,7 +106,7 @@ int fo_reorder_post_ep(const fo_plan *p, const void *reordered, void *out, const
 int fo_reorder_pre(const fo_plan *p, const void *in, void *reordered, hipStream_t stream) {
   if (!device_ready(p)) return FO_ERR_INVALID;
   if (!buf_ok(p, in) || !buf_ok(p, reordered)) return FO_ERR_INVALID;
-  return fo::launch_reorder(p, in, reordered, false, stream);
+  return fo::launch_reorder(p, in, reordered, false, 0, p->NT, stream);
 }
 
 int fo_stream_create(hipStream_t *out) {

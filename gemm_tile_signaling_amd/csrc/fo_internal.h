@@ -118,7 +118,8 @@ int launch_gemm(const fo_plan *p, const void *A, const void *B, void *C, bool ro
 int launch_consume(const fo_plan *p, const void *send, const void *peer, void *recv,
                    const uint32_t *sig, uint32_t epoch, int32_t g_begin, int32_t g_end,
                    int32_t *status, uint64_t timeout_ticks, int32_t grid, uint64_t *trace, hipStream_t s);
-int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajor, hipStream_t s);
+int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajor, int32_t slot_begin,
+                   int32_t slot_end, hipStream_t s);
 int launch_post_ep(const fo_plan *p, const void *src, void *dst, const void *bias, int act, hipStream_t s);
 
 }  // namespace fo

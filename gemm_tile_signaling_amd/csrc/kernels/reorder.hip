@@ -11,7 +11,8 @@
 //   post-communication reorder's pass, so the output is written once.
 //
 // Design: pure data movement, bound by HBM bandwidth.  One workgroup per
-// (slot, band of up to 128 tile rows); every row of a tile is a contiguous
+// (slot, band of up to 128 tile rows), over all slots or over the slots of a
+// range of groups (a group's slots are consecutive); every row of a tile is a contiguous
 // run of `cols` elements on both sides, so all accesses are 16-byte buffer
 // loads and stores with 32-bit offsets (the plan keeps M*N at most 2^30).  The
 // source and destination offset of each row are computed once into LDS;
@@ -40,6 +41,7 @@ struct ReorderParams {
   int32_t to_rowmajor;
   const uint16_t *bias;  // epilogue only: [problems][N], or NULL
   uint32_t bias_bytes;
+  int32_t slot0;         // first slot of the launch: workgroup (x, y) moves slot slot0 + x
 };
 
 template <int RPB, int CPR>  // rows per block, 16-byte chunks per tile row
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(ReorderParams p) {
   __shared__ uint32_t src_row[RPB], dst_row[RPB];  // byte offsets of each row's first element
   constexpr int kPer = RPB * CPR / kThreads;
   static_assert(RPB * CPR % kThreads == 0, "split");
-  const int slot = blockIdx.x;
+  const int slot = p.slot0 + blockIdx.x;
   const int r0 = blockIdx.y * RPB;
   const TileDesc t = p.slots[slot];
   const int tid = threadIdx.x;
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void post_ep_kernel(ReorderParams p) {
   __shared__ uint32_t src_row[RPB], dst_row[RPB];
   constexpr int kPer = RPB * CPR / kThreads;
   static_assert(RPB * CPR % kThreads == 0 && kThreads % CPR == 0, "split");
-  const int slot = blockIdx.x;
+  const int slot = p.slot0 + blockIdx.x;
   const int r0 = blockIdx.y * RPB;
   const TileDesc t = p.slots[slot];
   const int tid = threadIdx.x;
@@ -196,8 +198,10 @@ int launch_post_ep(const fo_plan *p, const void *src, void *dst, const void *bia
   return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
 }
 
-int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajor, hipStream_t s) {
-  if (p->NT == 0) return FO_OK;
+int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajor, int32_t slot_begin,
+                   int32_t slot_end, hipStream_t s) {
+  const int32_t nslots = slot_end - slot_begin;
+  if (nslots <= 0) return FO_OK;
   ReorderParams rp{};
   rp.src = static_cast<const uint16_t *>(src);
   rp.dst = static_cast<uint16_t *>(dst);
@@ -206,12 +210,13 @@ int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajo
   rp.N = p->N;
   rp.bytes = (uint32_t)(2 * p->M * p->N);
   rp.to_rowmajor = to_rowmajor ? 1 : 0;
+  rp.slot0 = slot_begin;
   if (p->BN == 128) {
     constexpr int RPB = 128;
-    hipLaunchKernelGGL((reorder_kernel<RPB, 16>), dim3(p->NT, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
+    hipLaunchKernelGGL((reorder_kernel<RPB, 16>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
   } else if (p->BN == 64) {
     constexpr int RPB = 64;
-    hipLaunchKernelGGL((reorder_kernel<RPB, 8>), dim3(p->NT, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
+    hipLaunchKernelGGL((reorder_kernel<RPB, 8>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
   } else {
     return FO_ERR_UNSUPPORTED;
   }

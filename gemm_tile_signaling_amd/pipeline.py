@@ -33,10 +33,13 @@ from . import Plan, stream_create, stream_destroy
 
 class Pipeline:
     def __init__(self, plan: Plan, A, B, peer, *, consumer_workgroups: int = 0, timeout_us: int = 0,
-                 in_place: bool = False):
+                 in_place: bool = False, post_per_group: bool = False):
         import torch
         self.torch = torch
         self.plan = plan
+        # post_per_group: the stream-B side runs consumer(g), post-reorder(g) for each group in turn,
+        # so a group's tiles go back in place while later groups are computed
+        self.post_per_group = post_per_group
         n = plan.M * plan.N
         dev = A.device
         self.A, self.B, self.peer = A, B, peer
@@ -103,16 +106,30 @@ class Pipeline:
             ev["gemm"][1].record(s_gemm)
         if "consume" in ev:
             ev["consume"][0].record(s_comm)
-        p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status,
-                        timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
-                        trace=consumer_trace, stream=s_comm)
-        if "consume" in ev:
-            ev["consume"][1].record(s_comm)
-        if "post" in ev:
-            ev["post"][0].record(s_comm)
-        p.reorder_post(self.recv, self.out, stream=s_comm)
-        if "post" in ev:
-            ev["post"][1].record(s_comm)
+        if self.post_per_group and p.P > 1:
+            # events: 'consume' spans the whole stream-B side, 'post' the last group's post-reorder
+            for g in range(p.P):
+                p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status, g_begin=g, g_end=g + 1,
+                                timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
+                                trace=consumer_trace, stream=s_comm)
+                if "post" in ev and g == p.P - 1:
+                    ev["post"][0].record(s_comm)
+                p.reorder_post(self.recv, self.out, stream=s_comm, groups=(g, g + 1))
+            if "consume" in ev:
+                ev["consume"][1].record(s_comm)
+            if "post" in ev:
+                ev["post"][1].record(s_comm)
+        else:
+            p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status,
+                            timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
+                            trace=consumer_trace, stream=s_comm)
+            if "consume" in ev:
+                ev["consume"][1].record(s_comm)
+            if "post" in ev:
+                ev["post"][0].record(s_comm)
+            p.reorder_post(self.recv, self.out, stream=s_comm)
+            if "post" in ev:
+                ev["post"][1].record(s_comm)
         self.post_stream = s_comm
         return e
 

@@ -266,6 +266,19 @@ int fo_consume_group(const fo_plan *plan, const void *send, const void *peer, vo
 int fo_reorder_post(const fo_plan *plan, const void *reordered, void *out, hipStream_t stream);
 
 /*
+ * The same inverse mapping restricted to the tiles of groups g_begin ..
+ * g_end-1: only their elements of out are written, the rest of out is left
+ * as it is (deep-dive 二 › 解决方案: 映射表重排 -- once a group's
+ * communication is done its span holds finished tiles, so they can be put
+ * back in place while later groups are still computed or communicated).
+ * Calls over a partition of [0, P) write out completely, as fo_reorder_post
+ * does.  0 <= g_begin <= g_end <= P, else FO_ERR_INVALID; an empty range
+ * enqueues nothing.  Buffers as for fo_reorder_post.
+ */
+int fo_reorder_post_groups(const fo_plan *plan, int32_t g_begin, int32_t g_end, const void *reordered, void *out,
+                           hipStream_t stream);
+
+/*
  * Post-communication reordering fused with the element-wise epilogue
  * (deep-dive 五 › Epilogue 集成: the operations that follow the GEMM -- bias
  * addition, ReLU, SiLU -- run in the reorder's pass, so the output is

@@ -83,6 +83,37 @@ def test_reorder_pre_post_bit_exact(entry):
     assert np.array_equal(to_host(r2), want_post)
 
 
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_reorder_post_by_groups(entry):
+    """fo_reorder_post_groups writes exactly the elements whose reordered offset lies in the
+    groups' spans (oracle spans) and leaves the rest of out untouched; one call per group
+    rebuilds the whole row-major output."""
+    from oracle.layout import group_spans
+    o, p = _plans(entry)
+    off = element_offsets(o).ravel()
+    spans = group_spans(o)
+    Y = random_bits(9, o.M * o.N, entry[4])
+    want = oracle.post_reorder(Y, off).ravel()
+    marker = 0x7FC0
+    dY = to_dev(Y)
+    say(f"reorder_post by groups {entry[0]} P={p.P}")
+    for g0, g1 in {(0, p.P), (0, 1), (p.P - 1, p.P), (p.P // 2, p.P // 2)}:
+        out = empty16(o.M * o.N, marker)
+        p.reorder_post(dY, out, groups=(g0, g1))
+        torch.cuda.synchronize()
+        inside = (off >= spans[g0]) & (off < spans[g1])
+        got = to_host(out)
+        assert np.array_equal(got[inside], want[inside]), (g0, g1)
+        assert np.all(got[~inside] == marker), (g0, g1)
+    out = empty16(o.M * o.N, marker)
+    for g in range(p.P):
+        p.reorder_post(dY, out, groups=(g, g + 1))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out), want)
+    with pytest.raises(fo.FoError):
+        p.reorder_post(dY, out, groups=(0, p.P + 1))
+
+
 # --------------------------------------------------------------------------- fused post-reorder epilogue
 
 @pytest.mark.parametrize("act", ["none", "relu", "silu"])

@@ -108,11 +108,13 @@ def test_serial_passes_between_overlapped_ones(entry):
 @pytest.mark.parametrize("entry", [e for e in PLANS if e[0] in ("ragged_256", "subtile_r4", "tiny_fp16")],
                          ids=lambda e: e[0])
 @pytest.mark.parametrize("in_place", [False, True])
-def test_back_to_back_passes_keep_recv_ordered(entry, in_place):
+@pytest.mark.parametrize("per_group", [False, True])
+def test_back_to_back_passes_keep_recv_ordered(entry, in_place, per_group):
     """Consecutive passes alternate between two peer buffers and write separate
     outputs, so a consumer that rewrote recv before the previous pass's
     post-reorder had read it would leave the other peer's sums in an output.
-    Every output is checked bit-exactly (ternary inputs) against the oracle."""
+    Every output is checked bit-exactly (ternary inputs) against the oracle,
+    with the post-reorder over the whole output or group by group."""
     o, p = _plans(entry)
     dt = entry[4]
     A, B, peer0 = _inputs(entry, dist=("ternary",), seed=620)
@@ -120,9 +122,9 @@ def test_back_to_back_passes_keep_recv_ordered(entry, in_place):
     want = [oracle.run_pipeline(A, B, pr, o, dt)["out"].ravel() for pr in (peer0, peer1)]
     assert not np.array_equal(want[0], want[1])
     n = 40
-    say(f"pipeline back-to-back {entry[0]}, {n} passes, in_place={in_place}")
+    say(f"pipeline back-to-back {entry[0]}, {n} passes, in_place={in_place}, post per group={per_group}")
     peers = [to_dev(peer0), to_dev(peer1)]
-    pipe = Pipeline(p, to_dev(A), to_dev(_stack(B)), peers[0], in_place=in_place)
+    pipe = Pipeline(p, to_dev(A), to_dev(_stack(B)), peers[0], in_place=in_place, post_per_group=per_group)
     outs = [torch.empty(o.M * o.N, dtype=torch.int16, device="cuda") for _ in range(n)]
     for i in range(n):
         pipe.peer = peers[i % 2]
