@@ -83,7 +83,7 @@ def wave_pattern_of(t_sig, W, tick_us, bins=40):
             "bin_us": round(float(edges[1] - edges[0]), 3), "histogram": hist}
 
 
-def configs_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
+def configs_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
     """The other workloads beside the headline: signaling and plain GEMM alone, and one pass of the
     pipeline at each workload's first partition (one wave per group if it names none).
 
@@ -92,7 +92,7 @@ def configs_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
     """
     from workloads import WORKLOADS, moe_routing
     out = []
-    s = torch.cuda.Stream(device=dev)
+    s = streams[0]
     td = {"bf16": torch.bfloat16, "fp16": torch.float16}
     for name in ("ar_prefill", "ar_decode", "rs", "moe_a2a"):
         w = WORKLOADS[name]
@@ -123,7 +123,7 @@ def configs_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
             _sig(s)
         sig_ms = _time_kernel(torch, _sig, s, 10)
         plain_ms = _time_kernel(torch, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, 10)
-        pipe = Pipeline(plan, dA, dB, dpeer)
+        pipe = Pipeline(plan, dA, dB, dpeer, streams=streams)
         for _ in range(warmup):
             pipe.step()
         pipe.join()
@@ -149,7 +149,7 @@ def configs_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
     return out
 
 
-def search_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
+def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
     """Predictive partition search against measurement on the 4-wave prefill workload.
 
     The search's offline inputs, as the pages describe them (deep-dive
@@ -167,7 +167,7 @@ def search_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
     dA = torch.from_numpy(A.view(np.int16).reshape(-1).copy()).to(dev)
     dB = torch.from_numpy(np.concatenate([b.reshape(-1) for b in B]).view(np.int16).copy()).to(dev)
     dpeer = torch.from_numpy(peer.view(np.int16).copy()).to(dev)
-    s = torch.cuda.Stream(device=dev)
+    s = streams[0]
     base = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W)
     C = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
     gemm_ms = float(np.median([_time_kernel(torch, lambda st: base.gemm_plain(dA, dB, C, stream=st), s, 1)
@@ -200,7 +200,7 @@ def search_check(torch, fo, Pipeline, dev, steps=20, warmup=5):
     for mask in range(1 << (base.T - 1)):
         comp = comp_of(mask, base.T)
         plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp)
-        pipe = Pipeline(plan, dA, dB, dpeer)
+        pipe = Pipeline(plan, dA, dB, dpeer, streams=streams)
         for _ in range(warmup):
             pipe.step()
         evs = [{k: _event_pairs(torch, 1)[0] for k in ("gemm", "consume", "post")} for _ in range(steps)]
@@ -350,12 +350,23 @@ def main():
                           "calibration_copy_bytes": 256 * 2 ** 20, "status": int(status.item())}), flush=True)
         return
 
-    pipes = []
+    # one pair of streams, each with a hardware queue of its own, for every pipeline and every kernel
+    # timed alone: the device has few hardware queues, and streams created per pipeline would share
+    # them in an order that changes the timings from one schedule to the next
+    streams = (fo.stream_create(), fo.stream_create())
+    pipes = []   # one per schedule: a partition, with the post-reorder whole or group by group
     for comp in comps:
         plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W,
                        composition=comp, mode=w.mode, ranks=w.ranks, row_dest=row_dest)
-        pipes.append(dict(plan=plan, pipe=Pipeline(plan, dA, dB, dpeer), comp=comp or tuple([1] * plan.T)))
+        for per_group in ((False, True) if plan.P > 1 else (False,)):
+            pipes.append(dict(plan=plan, pipe=Pipeline(plan, dA, dB, dpeer, post_per_group=per_group,
+                                                       streams=streams),
+                              comp=comp or tuple([1] * plan.T), per_group=per_group))
     launches = [0]   # signaling-GEMM launches so far (locates the timed region in a kernel trace)
+    # every event is created here: creating a few hundred takes tens of milliseconds, and the GPU
+    # idling that long between the warm-up and the timed passes starts them in a clock transient
+    gemm_ev = _event_pairs(torch, a.steps)
+    br_ev = [{k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")} for _ in pipes]
 
     def passes(pipe, n, **kw):
         for _ in range(n):
@@ -366,11 +377,11 @@ def main():
         if int(pipe.status.item()) != 0:
             raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
 
-    # choose the partition: short blocks of passes, every schedule in turn, three rounds, so that
+    # choose the partition: blocks of K passes, every schedule in turn, three rounds, so that
     # clock and power drift falls on all of them alike; the serial schedule (GEMM, then consumer,
     # then post-reorder, one queue) is measured the same way for comparison
     passes(pipes[0]["pipe"], a.warmup)
-    n_pick = max(10, a.steps // 2)
+    n_pick = a.steps
     sched = [(i, False) for i in range(len(pipes))] + [(0, True)]
     picks = {k: [] for k in sched}
     for _ in range(3):
@@ -389,7 +400,6 @@ def main():
     # events (on its own stream), since every event is a packet in a hardware queue and adds to the pass
     passes(pipe, a.warmup)
     timed_first = launches[0]
-    gemm_ev = _event_pairs(torch, a.steps)
     t0 = time.perf_counter()
     for i in range(a.steps):
         pipe.step(events={"gemm": gemm_ev[i]})
@@ -405,8 +415,7 @@ def main():
     timed_range = [timed_first, launches[0]]
 
     # untimed: every kernel of every partition bracketed, for the breakdown
-    for r in pipes:
-        evs = {k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")}
+    for r, evs in zip(pipes, br_ev):
         for i in range(a.steps):
             r["pipe"].step(events={k: v[i] for k, v in evs.items()})
         launches[0] += a.steps
@@ -432,7 +441,7 @@ def main():
     wave_pattern = wave_pattern_of(t_sig, plan.W, tick_us)
 
     # kernels alone (same plan), each timed with HIP events on its own stream
-    s = torch.cuda.Stream(device=dev)
+    s = streams[0]
     n_alone = max(10, min(a.steps, 50))
     C = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
     plain_ms = _time_kernel(torch, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, n_alone)
@@ -482,9 +491,10 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: GEMM M={w.M} N={w.N} K={w.K} {w.dtype}, {w.BM}x{w.BN} tiles, "
                                f"swizzle {w.S}, wave {w.W} tiles, groups {tuple(best['comp'])}, "
-                               f"consumer copy+add, post-reorder",
+                               f"consumer copy+add, post-reorder{' per group' if best['per_group'] else ''}",
                    "M": w.M, "N": w.N, "K": w.K, "tile": [w.BM, w.BN], "swizzle": w.S, "wave": w.W,
-                   "tiles": plan.NT, "waves": plan.T, "groups": list(best["comp"]), "parallelism": "1 GPU"},
+                   "tiles": plan.NT, "waves": plan.T, "groups": list(best["comp"]),
+                   "post_per_group": best["per_group"], "parallelism": "1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(w.name),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
@@ -507,16 +517,17 @@ def main():
         "signal_to_consume_us": signal_to_consume_us,
         "first_group_consumed_before_gemm_end_us": first_consume_before_gemm_end_us,
         "wave_pattern": wave_pattern,
-        "partitions": [{"groups": list(r["comp"]), "pick_step_ms": round(r["pick_ms"], 4),
+        "partitions": [{"groups": list(r["comp"]), "post_per_group": r["per_group"],
+                        "pick_step_ms": round(r["pick_ms"], 4),
                         "gemm_ms": round(r["br_gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
                         "post_ms": round(r["post_ms"], 4)} for r in pipes],
         "timed_signal_gemm_launches": timed_range,
         "cpu_baseline": None,
     }
     if not a.no_configs:
-        line["configs"] = configs_check(torch, fo, Pipeline, dev)
+        line["configs"] = configs_check(torch, fo, Pipeline, dev, streams)
     if not a.no_search:
-        line["search"] = search_check(torch, fo, Pipeline, dev)
+        line["search"] = search_check(torch, fo, Pipeline, dev, streams)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, peer, m_per, row_dest, best["comp"])
     print(json.dumps(line), flush=True)

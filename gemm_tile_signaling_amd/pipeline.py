@@ -33,7 +33,7 @@ from . import Plan, stream_create, stream_destroy
 
 class Pipeline:
     def __init__(self, plan: Plan, A, B, peer, *, consumer_workgroups: int = 0, timeout_us: int = 0,
-                 in_place: bool = False, post_per_group: bool = False):
+                 in_place: bool = False, post_per_group: bool = False, streams: Optional[tuple] = None):
         import torch
         self.torch = torch
         self.plan = plan
@@ -48,10 +48,17 @@ class Pipeline:
         self.out = torch.empty(n, dtype=torch.int16, device=dev)
         self.sig = plan.new_sig(dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
-        # each side gets a hardware queue of its own, or the consumer would run after the GEMM
-        with torch.cuda.device(dev):
-            self.sa = stream_create()
-            self.sb = stream_create()
+        # each side gets a hardware queue of its own, or the consumer would run after the GEMM.
+        # streams=(sa, sb): a pair from stream_create() shared with other pipelines (the caller
+        # destroys it); the device has few hardware queues, and pipelines with a pair each can
+        # end up with both sides of one pair on the same queue
+        self.own_streams = streams is None
+        if streams is None:
+            with torch.cuda.device(dev):
+                self.sa = stream_create()
+                self.sb = stream_create()
+        else:
+            self.sa, self.sb = streams
         self.epoch = 0
         self.consumer_workgroups = consumer_workgroups
         self.timeout_us = timeout_us
@@ -67,8 +74,9 @@ class Pipeline:
         if getattr(self, "sa", None) is not None:
             self.sa.synchronize()
             self.sb.synchronize()
-            stream_destroy(self.sa)
-            stream_destroy(self.sb)
+            if self.own_streams:
+                stream_destroy(self.sa)
+                stream_destroy(self.sb)
             self.sa = self.sb = None
 
     def __del__(self):
