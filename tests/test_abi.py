@@ -64,6 +64,7 @@ def test_enqueue_on_host_only_plan_is_rejected():
     assert _code(lambda: p.gemm_plain(16, 16, 16, stream=0)) == -1
     assert _code(lambda: p.consume_group(16, 16, 16, 16, 1, 16, stream=0)) == -1
     assert _code(lambda: p.reorder_post(16, 16, stream=0)) == -1
+    assert _code(lambda: p.reorder_post(16, 16, groups=(0, 1), stream=0)) == -1
     assert _code(lambda: p.reorder_pre(16, 16, stream=0)) == -1
     assert p.info["device"] == -1
 
