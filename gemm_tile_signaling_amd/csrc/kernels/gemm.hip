@@ -22,7 +22,8 @@
 //     output row, which the epilogue writes as 8-byte pieces.
 //   * BK = 64; A and B K-slices go from memory straight into LDS (gfx950
 //     buffer loads with the LDS destination, 16 bytes per lane), through a
-//     ring of three LDS stages: slice k+2 is loaded while slice k is
+//     ring of LDS stages (three; six for 64 x 64 tiles, which have little
+//     arithmetic per slice to hide a load behind): slice k+2 (k+5) is loaded while slice k is
 //     multiplied, its DMA instructions spread over the multiplication so the
 //     wave never waits on a full memory queue with the matrix pipe idle; no
 //     VGPRs or ds_write instructions are spent on staging.
@@ -76,10 +77,24 @@ constexpr int BK = 64;
 constexpr int kRowBytes = BK * 2;               // one staged row of A or B
 constexpr int kVmcntZero = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 constexpr int kLgkmcntZero = 0xC07F;            // s_waitcnt lgkmcnt(0), other counters unconstrained
-constexpr int kStages = 3;                      // LDS ring depth of the main loop
 
 // s_waitcnt immediate for vmcnt(n) with the other counters unconstrained (gfx9 encoding)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+
+// Wait until at most min(s, S) K-slices of LOADS loads each are still in
+// flight (s is wave-uniform; the waits need immediates, hence the chain).
+template <int LOADS, int S>
+__device__ __forceinline__ void wait_slices(int s) {
+  if constexpr (S > 0) {
+    if (s >= S) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(S * LOADS));
+      return;
+    }
+    wait_slices<LOADS, S - 1>(s);
+  } else {
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  }
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -197,6 +212,10 @@ __device__ __forceinline__ bool wave_snapshot(const GemmParams &p, int w) {
 
 template <int BM, int BN>
 struct Cfg {
+  // LDS ring depth: slice k+NS-1 is loaded while slice k is multiplied.  Small
+  // tiles have little arithmetic per slice, so they keep more slices in flight.
+  static constexpr int NS = BM == 64 ? 6 : 3;
+  static constexpr int DIST = NS - 1;                 // prefetch distance in slices
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_PER_T = BM * 8 / kThreads;  // 16-byte chunks per thread per stage
@@ -206,10 +225,11 @@ struct Cfg {
   static constexpr int OUT_PITCH = BN * 2 + 16;      // bytes per staged output row
   static constexpr int OUT_BYTES = BM * OUT_PITCH;
   static constexpr int ROWOFF = OUT_BYTES;           // int64 per row after the staging tile
-  static constexpr int LDS = (kStages * STAGE > OUT_BYTES + BM * 8) ? kStages * STAGE : OUT_BYTES + BM * 8;
+  static constexpr int LDS = (NS * STAGE > OUT_BYTES + BM * 8) ? NS * STAGE : OUT_BYTES + BM * 8;
   static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "chunk split");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
   static_assert(LOADS % 4 == 0, "a slice's DMA instructions split over four blocks");
+  static_assert(NS * LOADS <= 63, "loads in flight fit the vmcnt counter");
 };
 
 // SIGNAL: the signaling GEMM (reordered stores, counting table, flags); otherwise
@@ -256,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   int64_t *rowoff = reinterpret_cast<int64_t *>(smem + C::ROWOFF);
 
   // The tile a workgroup works on and its buffer resources.  A tile's first
-  // two K-slices are issued as soon as the previous tile's staging area is
+  // NS-1 K-slices are issued as soon as the previous tile's staging area is
   // free, before that tile's signal, so the signal's waits overlap them.
   TileDesc t = p.slots[0];
   __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, 0), rb = make_rsrc(p.B, 0);
@@ -265,10 +285,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     ra = make_rsrc(p.A + (int64_t)t.row0 * p.K, t.rows * row_bytes);
     rb = make_rsrc(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K, t.cols * row_bytes);
   };
-  // K-slice kt -> LDS stage kt % 3, as C::LOADS DMA instructions per thread;
+  // K-slice kt -> LDS stage kt % NS, as C::LOADS DMA instructions per thread;
   // part p of 4 issues instructions [p * DPB, (p + 1) * DPB)
   constexpr int DPB = C::LOADS / 4;
-  auto stage_dst = [&](int kt) { return smem + (kt % kStages) * C::STAGE + wave * 1024; };
+  auto stage_dst = [&](int kt) { return smem + (kt % C::NS) * C::STAGE + wave * 1024; };
 #define FO_DMA_PART(PART, KT)                                                                              \
   dma_part<PART, DPB, C::A_PER_T, C::B_PER_T>(ra, rb, stage_dst(KT), s_bofs, g_base, g_step,              \
                                               (uint32_t)(KT) * kRowBytes)
@@ -278,9 +298,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     FO_DMA_PART(2, kt);
     FO_DMA_PART(3, kt);
   };
-  auto prologue = [&]() {  // slices 0 and 1 of the current tile
-    issue(0);
-    if (nk > 1) issue(1);
+  auto prologue = [&]() {  // slices 0 .. NS-2 of the current tile
+#pragma unroll
+    for (int kt = 0; kt < C::DIST; ++kt)
+      if (kt < nk) issue(kt);
   };
   if (pos < p.NT) {
     load_tile(pos);
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // in the order the MFMAs below consume them.
     u32x4 fa[2][C::FM], fb[2][C::FN];
     auto read_frags = [&](int u, int stage, int ks) {
-      const char *base = smem + (stage % kStages) * C::STAGE;
+      const char *base = smem + (stage % C::NS) * C::STAGE;
       const uint32_t chunk = (uint32_t)(((ks * 2 + frag_half) ^ swz) << 4);
       fa[u][0] = *reinterpret_cast<const u32x4 *>(base + a_frag + chunk);
 #pragma unroll
@@ -345,31 +366,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Stage s holds slice s from when it is loaded (during slice s-2) until
-    // its last fragments are read (third k-step of slice s): three LDS stages.
-    // Slice kt+2's loads are spread over the four blocks of slice kt.  Slices
-    // 0 and 1 were issued ahead (prologue); anything this wave issued before
-    // them (the previous tile's stores) is older, so the same count holds.
-    if (nk > 1) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
-    } else {
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    }
+    // Stage s % NS holds slice s from when it is loaded (during slice s-D, D =
+    // NS-1) until its last fragments are read (third k-step of slice s).
+    // Slice kt+D's loads are spread over the four blocks of slice kt.  Slices
+    // 0 .. D-1 were issued ahead (prologue); anything this wave issued before
+    // them (the previous tile's stores) is older, so the same counts hold:
+    // slice 0 has landed once at most min(D-1, nk-1) slices are in flight.
+    constexpr int D = C::DIST;
+    wait_slices<C::LOADS, D - 1>(nk - 1);
     bare_barrier();
     read_frags(0, 0, 0);
     // The last slice is peeled off so that the loop body has no join point at
     // which the wait-count insertion would have to assume the worst of two paths.
-    auto three_blocks_dma = [&](int kt) {  // and three quarters of slice kt+2's loads
+    auto three_blocks_dma = [&](int kt) {  // and three quarters of slice kt+D's loads
       __builtin_amdgcn_sched_barrier(0);
-      FO_DMA_PART(0, kt + 2);
+      FO_DMA_PART(0, kt + D);
       read_frags(1, kt, 1);
       mfmas(0);
       block_order_dma();
-      FO_DMA_PART(1, kt + 2);
+      FO_DMA_PART(1, kt + D);
       read_frags(0, kt, 2);
       mfmas(1);
       block_order_dma();
-      FO_DMA_PART(2, kt + 2);
+      FO_DMA_PART(2, kt + D);
       read_frags(1, kt, 3);
       mfmas(0);
       block_order_dma();
@@ -389,25 +408,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // Steady state: one path per iteration, so the accumulators keep their
     // registers from one iteration to the next.
     int kt = 0;
-    for (; kt + 2 < nk; ++kt) {
+    for (; kt + D < nk; ++kt) {
       three_blocks_dma(kt);
-      FO_DMA_PART(3, kt + 2);
-      // this wave's reads of slice kt are complete and its loads of slice kt+1 landed
+      FO_DMA_PART(3, kt + D);
+      // this wave's reads of slice kt are complete and its loads of slice kt+1
+      // landed (slices kt+2 .. kt+D may still be in flight)
       __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * C::LOADS));
       bare_barrier();  // no wave reads slice kt any more; slice kt+1 is in LDS for every wave
       read_frags(0, kt + 1, 0);
       mfmas(1);
       block_order();
     }
-    if (kt + 1 < nk) {  // the last handover: nothing left to load
+    // the last handovers: nothing left to load, slices kt+2 .. nk-1 in flight
+    auto drain = [&](int kt) {
       three_blocks(kt);
       __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      wait_slices<C::LOADS, D - 2>(nk - 2 - kt);
       bare_barrier();
       read_frags(0, kt + 1, 0);
       mfmas(1);
       block_order();
+    };
+    if constexpr (D == 2) {
+      if (kt + 1 < nk) drain(kt++);
+    } else {
+      for (; kt + 1 < nk; ++kt) drain(kt);
     }
     three_blocks(nk - 1);
     mfmas(1);
@@ -456,10 +482,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     if constexpr (SIGNAL) {
       if (!more)
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      else if (nk > 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::LOADS));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LOADS));
+      else  // the next tile's min(D, nk) slices were issued after the stores
+        wait_slices<C::LOADS, C::DIST>(nk);
       __syncthreads();
       if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
