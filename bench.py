@@ -245,11 +245,11 @@ def _time_kernel(torch, launch, stream, n, scratch=None):
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the GEMM kernel's sources: ties committed traffic counters to the code they measured."""
+    """sha256 over the GEMM kernel's sources and build flags: ties committed traffic counters to the code they measured."""
     import hashlib
     h = hashlib.sha256()
     for rel in ("gemm_tile_signaling_amd/csrc/kernels/gemm.hip", "gemm_tile_signaling_amd/csrc/kernels/buffer.h",
-                "gemm_tile_signaling_amd/csrc/fo_internal.h"):
+                "gemm_tile_signaling_amd/csrc/fo_internal.h", "gemm_tile_signaling_amd/build.py"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
