@@ -25,12 +25,13 @@ fo = pytest.importorskip("gemm_tile_signaling_amd")
 torch = pytest.importorskip("torch")
 from gemm_tile_signaling_amd.pipeline import Pipeline  # noqa: E402
 
+# (workload, partition, post-reorder group by group) -- the benchmark's schedules among them
 CASES = [
-    ("profiled", (2,)), ("profiled", (1, 1)),
-    ("ar_prefill", (1, 1, 1, 1)), ("ar_prefill", (2, 2)), ("ar_prefill", (1, 3)),
-    ("ar_decode", (1,)),
-    ("rs", (1, 1, 1, 1)), ("rs", (1, 2, 1)),
-    ("moe_a2a", (4, 4, 4, 5)), ("moe_a2a", (1,) * 17),
+    ("profiled", (2,), False), ("profiled", (1, 1), False), ("profiled", (1, 1), True),
+    ("ar_prefill", (1, 1, 1, 1), True), ("ar_prefill", (2, 2), False), ("ar_prefill", (1, 3), False),
+    ("ar_decode", (1,), False),
+    ("rs", (1, 1, 1, 1), False), ("rs", (1, 2, 1), True),
+    ("moe_a2a", (4, 4, 4, 5), True), ("moe_a2a", (1,) * 17, False),
 ]
 
 _cache = {}
@@ -60,8 +61,9 @@ def _samples(o, seed, n=3000):
     return np.array(rows), np.array(cols)
 
 
-@pytest.mark.parametrize("name,comp", CASES, ids=[f"{n}-{'.'.join(map(str, c))}" for n, c in CASES])
-def test_workload_full_size(name, comp):
+@pytest.mark.parametrize("name,comp,per_group", CASES,
+                         ids=[f"{n}-{'.'.join(map(str, c))}{'-pg' if g else ''}" for n, c, g in CASES])
+def test_workload_full_size(name, comp, per_group):
     w, A, B, peer, m_per, row_dest = _inputs(name)
     o = make_plan(m_per, w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=comp, mode=w.mode, ranks=w.ranks,
                   row_dest=row_dest)
@@ -70,9 +72,9 @@ def test_workload_full_size(name, comp):
     assert (p.NT, p.T, p.P) == (o.NT, o.T, o.P)
     rows, cols = _samples(o, 1)
     s = oracle.sample_outputs(A, B, peer, o, w.dtype, rows, cols)
-    say(f"workload {name} comp={comp} M={o.M} N={o.N} K={w.K} NT={o.NT} T={o.T}")
+    say(f"workload {name} comp={comp} post per group={per_group} M={o.M} N={o.N} K={w.K} NT={o.NT} T={o.T}")
     dA, dB, dpeer = to_dev(A), to_dev(np.concatenate([b.reshape(-1) for b in B])), to_dev(peer)
-    pipe = Pipeline(p, dA, dB, dpeer)
+    pipe = Pipeline(p, dA, dB, dpeer, post_per_group=per_group)
     pipe.step()
     pipe.step()
     pipe.join()
