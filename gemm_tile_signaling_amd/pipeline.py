@@ -1,7 +1,10 @@
 """One pass of the hot path on two HIP streams, built from the C-ABI calls.
 
 One stream runs the signaling GEMM; the other runs the consumer and then the
-post-communication reorder.  The two are linked on the device only through
+post-communication reorder, over the whole output or group by group
+(consumer(g), then the reorder of g's tiles, for each group in turn, so the
+first groups are back in row-major order while the GEMM still computes the
+last ones).  The two are linked on the device only through
 the signal words (counting table + flags).  Passes are kept in order: a
 pass's GEMM starts after the previous pass's post-reorder, as a layer's GEMM
 waits for the previous layer's output.  The two streams swap roles every
