@@ -12,7 +12,13 @@ namespace {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-bool device_ready(const fo_plan *p) { return p && !p->host_only && p->dev_block; }
+// a plan with device tables, whose device is the current one (its table
+// pointers mean nothing on another device)
+bool device_ready(const fo_plan *p) {
+  if (!p || p->host_only || !p->dev_block) return false;
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == p->device;
+}
 
 // a buffer of M*N elements must be present and 16-byte aligned unless it is empty
 bool buf_ok(const fo_plan *p, const void *ptr) { return (p->M * p->N == 0) || (ptr && aligned16(ptr)); }

@@ -27,7 +27,9 @@
  *     asynchronous on the given HIP stream; they neither allocate nor copy
  *     from the host nor synchronise.  Errors they return are detected on the
  *     host before any launch; errors that arise on the device are written to
- *     a caller-provided status word.
+ *     a caller-provided status word.  They need the plan's device to be the
+ *     current HIP device (FO_ERR_INVALID otherwise), and the stream and
+ *     buffers to belong to it.
  *   - Element types: FO_BF16 or FO_FP16 for A, B and every output buffer.
  *     Accumulation is fp32; results are rounded to the element type,
  *     round-to-nearest-even.
