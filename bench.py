@@ -301,7 +301,7 @@ def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, min_seconds=10.0):
 def main():
     a = _args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {a.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {a.gpus}",
               file=sys.stderr)
         sys.exit(2)
     import torch

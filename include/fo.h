@@ -47,7 +47,7 @@ extern "C" {
 typedef enum fo_status {
   FO_OK = 0,
   FO_ERR_INVALID = -1,      /* bad argument: null or misaligned pointer, bad sizes, bad partition */
-  FO_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement (e.g. K % 64 != 0)  */
+  FO_ERR_UNSUPPORTED = -2,  /* valid request the library does not implement (e.g. K % 64 != 0)*/
   FO_ERR_HIP = -3,          /* a HIP runtime call failed                                       */
   FO_ERR_NOMEM = -4,        /* host or device allocation failed at plan creation               */
   FO_ERR_TIMEOUT = -5       /* device-side: the consumer waited longer than its time limit     */
