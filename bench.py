@@ -8,13 +8,16 @@ synthetic and already resident in HBM when the timed region starts.
 
 Default workload: the profiled GEMM shape of the pages' wave-pattern figure,
 M = 2048, N = K = 8192, bf16, 256 x 128 tiles, 512 tiles over 256 CUs (two
-waves), partitions (2) and (1, 1).  ``value`` is useful GEMM TFLOP/s of the
-whole step (2 M N K per step / step time) for the best partition.
+waves), partitions (2) and (1, 1), the latter also with the post-reorder run
+group by group.  ``value`` is useful GEMM TFLOP/s of the whole step
+(2 M N K per step / step time) for the best of these schedules.
 
 Prints one JSON line.  Extra fields: the signaling and plain GEMMs measured
-alone, their ratio, the consumer's and the post-reorder's HBM GB/s (MALL
-flushed before each timed launch), per-partition step rates, and the oracle
-timed on the host cores as a CPU baseline (rank 0, N = 1).
+alone (alternating blocks), their ratio, the consumer's and the
+post-reorder's HBM GB/s (MALL flushed before each timed launch), per-schedule
+pass times, the same pass without overlap, the other workloads, a check of
+the partition search, and the oracle timed on the host cores as a CPU
+baseline (rank 0, N = 1).
 """
 
 from __future__ import annotations
@@ -121,8 +124,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
             plan.gemm_signal(dA, dB, C, sig, ep[0], stream=st)
         for _ in range(3):
             _sig(s)
-        sig_ms = _time_kernel(torch, _sig, s, 10)
-        plain_ms = _time_kernel(torch, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, 10)
+        sig_ms, plain_ms = _time_pair(torch, _sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, 10)
         pipe = Pipeline(plan, dA, dB, dpeer, streams=streams)
         for _ in range(warmup):
             pipe.step()
@@ -228,6 +230,16 @@ def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
         "candidates": [{"groups": list(c), "predicted_us": round(p * 1e3, 1), "measured_us": round(m * 1e3, 1)}
                        for c, p, m in rows],
     }
+
+
+def _time_pair(torch, launch_a, launch_b, stream, n, rounds=3):
+    """Average durations (ms) of two launches timed in alternating blocks of n (median block of each over
+    `rounds` rounds), so that clock and power drift falls on both alike."""
+    a, b = [], []
+    for _ in range(rounds):
+        a.append(_time_kernel(torch, launch_a, stream, n))
+        b.append(_time_kernel(torch, launch_b, stream, n))
+    return float(np.median(a)), float(np.median(b))
 
 
 def _time_kernel(torch, launch, stream, n, scratch=None):
@@ -444,14 +456,14 @@ def main():
     s = streams[0]
     n_alone = max(10, min(a.steps, 50))
     C = torch.empty(w.M * w.N, dtype=torch.int16, device=dev)
-    plain_ms = _time_kernel(torch, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, n_alone)
     sig = plan.new_sig(dev)
     ep = [0]
 
     def _sig(st):
         ep[0] += 1
         plan.gemm_signal(dA, dB, pipe.buf, sig, ep[0], stream=st)
-    signal_ms = _time_kernel(torch, _sig, s, n_alone)
+    signal_ms, plain_ms = _time_pair(torch, _sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s,
+                                     max(10, n_alone // 3))
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     ready = plan.new_sig(dev)
     plan.flag_of(ready).fill_(1)
