@@ -27,6 +27,10 @@ Modules
               reorder patterns, pre- and post-communication reordering.
 ``pipeline``  the whole path end to end, and single-output sampling for
               full-size checks.
+``rowexchange`` the ReduceScatter + AllGather pattern: every rank's row shard
+              and the block-cyclic row exchange after the AllGather.
+``search``    the predictive wave-group partition search.
+``epilogue``  the post-communication reorder with bias and activation.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against the pages' worked examples, closed forms, invariants or brute force.
