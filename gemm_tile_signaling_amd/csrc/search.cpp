@@ -6,7 +6,7 @@
 //   scored by a latency model instead of being run -- per group, computation
 //   takes the GEMM's duration / T per wave and communication a latency read
 //   off a sampled latency-versus-size curve; a group's communication starts
-//   once both the computation up to it and the previous communication are
+//   once both its own computation and the previous group's communication are
 //   done.  The smallest predicted end of the last communication wins.
 //
 // Readings taken where the pages leave a step open: the first group has no
@@ -79,25 +79,21 @@ extern "C" int fo_plan_search(const fo_plan *p, double gemm_seconds, const doubl
   double best = 0.0;
   uint32_t best_mask = 0;
   for (uint32_t mask = 0; mask < candidates; ++mask) {
-    double t_acc_p = 0.0, t_acc_m = 0.0, prev_bytes = 0.0, bytes = 0.0;
-    int waves = 0, group = 0;
+    // comm_end(i) = max(compute_end(i), comm_end(i-1)) + latency(bytes of group i), comm_end(-1) = 0
+    double comm_end = 0.0, bytes = 0.0;
+    int waves_done = 0;
     for (int w = 0; w < T; ++w) {
       bytes += wave_bytes[w];
-      ++waves;
-      if (w == T - 1 || ((mask >> w) & 1u)) {  // group ends after wave w+1
-        const double t_m = group > 0 ? curve.latency(prev_bytes) : 0.0;
-        t_acc_m = std::max(t_acc_p, t_acc_m) + t_m;
-        t_acc_p = t_acc_p + per_wave * waves;
-        prev_bytes = bytes;
+      ++waves_done;
+      if (w == T - 1 || ((mask >> w) & 1u)) {  // a group ends after wave w+1
+        const double compute_end = per_wave * waves_done;
+        comm_end = std::max(compute_end, comm_end) + curve.latency(bytes);
         bytes = 0.0;
-        waves = 0;
-        ++group;
       }
     }
-    t_acc_m = std::max(t_acc_p, t_acc_m) + curve.latency(prev_bytes);
-    if (all_seconds) all_seconds[mask] = t_acc_m;
-    if (mask == 0 || t_acc_m < best) {
-      best = t_acc_m;
+    if (all_seconds) all_seconds[mask] = comm_end;
+    if (mask == 0 || comm_end < best) {
+      best = comm_end;
       best_mask = mask;
     }
   }

@@ -6,19 +6,20 @@ Method: deep-dive 四、实时调优 › 在线阶段: 预测搜索算法 and it
 (Grouping Tuning Algorithm).  For a candidate partition G = (G_1 .. G_P) of
 the T waves, each group's computation takes the GEMM's duration / T per wave;
 its communication takes a latency read off a sampled latency-versus-size
-curve.  Walking the groups in order, the communication of group i-1 starts
-when both the computation of groups up to i-1 and the previous
-communication are done; the prediction is the time the last group's
-communication ends.  The search evaluates every candidate and keeps the
-smallest prediction.
+curve.  A group's communication starts when both its own computation and
+the previous group's communication are done; the prediction is the time the
+last group's communication ends.  The search evaluates every candidate and
+keeps the smallest prediction.  (The page's listing evaluates group i-1's
+communication inside the step for group i and adds the last group's after
+the loop; the recurrence below is that computation written per group.)
 
 Readings:
-* the first group has nothing to communicate before it (the pages evaluate
-  the previous group's size inside the loop, which has no predecessor at the
-  first group): its communication term is zero;
+* nothing is communicated before the first group's computation ends (the
+  listing reads the previous group's size in the step of the first group,
+  which has no predecessor);
 * the last group's communication also waits for the end of the computation
-  and of the previous communication (the max stated for every other group;
-  the final line of the printed listing omits it);
+  and of the previous communication (the max the page states for every
+  group; the listing's closing step leaves it out);
 * the curve is a list of samples (bytes_k, seconds_k), bytes strictly
   increasing: latency is interpolated linearly in bytes between samples,
   equals the first sample's latency below it (a fixed per-call cost) and
@@ -72,18 +73,25 @@ def group_bytes(composition: Sequence[int], wave_bytes: Sequence[float]) -> List
 
 def predict(composition: Sequence[int], wave_bytes: Sequence[float], duration: float,
             curve_bytes: Sequence[float], curve_seconds: Sequence[float]) -> float:
-    """Predicted end of the last group's communication for one candidate."""
-    T = len(wave_bytes)
+    """Predicted end of the last group's communication for one candidate.
+
+    Group i's computation is done once the waves of groups 0..i are, at
+    ``compute_end = duration * (waves so far) / T``.  Its communication starts
+    when both that and the previous group's communication are done, and
+    lasts the latency of its span:
+
+        comm_end(i) = max(compute_end(i), comm_end(i - 1)) + latency(bytes of group i)
+
+    with comm_end(-1) = 0; the prediction is comm_end of the last group.
+    """
     sizes = group_bytes(composition, wave_bytes)
-    t_acc_p = 0.0     # computation finished so far
-    t_acc_m = 0.0     # communication finished so far
-    for i, c in enumerate(composition):
-        t_m = interp_latency(curve_bytes, curve_seconds, sizes[i - 1]) if i > 0 else 0.0
-        t_p = duration / T * c
-        t_acc_m = max(t_acc_p, t_acc_m) + t_m
-        t_acc_p = t_acc_p + t_p
-    t_acc_m = max(t_acc_p, t_acc_m) + interp_latency(curve_bytes, curve_seconds, sizes[-1])
-    return t_acc_m
+    per_wave = duration / len(wave_bytes)
+    waves_done, comm_end = 0, 0.0
+    for waves, size in zip(composition, sizes):
+        waves_done += waves
+        compute_end = per_wave * waves_done
+        comm_end = max(compute_end, comm_end) + interp_latency(curve_bytes, curve_seconds, size)
+    return comm_end
 
 
 def search(wave_bytes: Sequence[float], duration: float, curve_bytes: Sequence[float],
