@@ -9,7 +9,8 @@ buffer.
 
 The names follow the C ABI in ``include/fo.h``: ``Plan`` wraps
 ``fo_plan_groups``; its methods ``gemm_signal``, ``gemm_plain``,
-``consume_group``, ``reorder_post``, ``reorder_post_ep`` and ``reorder_pre``
+``consume_group``, ``consume_group_gated``, ``reorder_post``,
+``reorder_post_ep``, ``reorder_pre``, ``reorder_shards`` and ``row_exchange``
 wrap the enqueue calls of the same names, and ``search`` wraps
 ``fo_plan_search``.
 """
@@ -23,15 +24,20 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["Plan", "FoError", "lib", "LIB_PATH", "status_string", "stream_create", "stream_destroy",
-           "FO_OK", "FO_ERR_INVALID", "FO_ERR_UNSUPPORTED", "FO_ERR_HIP", "FO_ERR_NOMEM", "FO_ERR_TIMEOUT"]
+           "arch_supported", "FO_OK", "FO_ERR_INVALID", "FO_ERR_UNSUPPORTED", "FO_ERR_HIP", "FO_ERR_NOMEM",
+           "FO_ERR_TIMEOUT", "FO_ERR_STALE"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
+# FO_LIB names another build of the same library (the sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("FO_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfo.so")
 
-FO_OK, FO_ERR_INVALID, FO_ERR_UNSUPPORTED, FO_ERR_HIP, FO_ERR_NOMEM, FO_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
+FO_OK, FO_ERR_INVALID, FO_ERR_UNSUPPORTED, FO_ERR_HIP, FO_ERR_NOMEM, FO_ERR_TIMEOUT, FO_ERR_STALE = \
+    0, -1, -2, -3, -4, -5, -6
 _DTYPES = {"bf16": 0, "fp16": 1}
 _MODES = {"tile": 0, "subtile": 1, "subtoken": 2}
 _ACTS = {"none": 0, "relu": 1, "silu": 2}
+_B_LAYOUTS = {"nk": 0, "kn": 1}
 FO_PLAN_HOST_ONLY = 1
+FO_PLAN_EPOCH_STAMPS = 2
 
 
 class FoError(RuntimeError):
@@ -47,7 +53,7 @@ class _Desc(C.Structure):
         ("dtype", C.c_int32), ("BM", C.c_int32), ("BN", C.c_int32), ("swizzle", C.c_int32),
         ("wave_size", C.c_int32), ("num_groups", C.c_int32), ("waves_per_group", C.POINTER(C.c_int32)),
         ("mode", C.c_int32), ("ranks", C.c_int32), ("row_dest", C.POINTER(C.c_int32)),
-        ("dispatch_order", C.POINTER(C.c_int32)), ("flags", C.c_uint32),
+        ("dispatch_order", C.POINTER(C.c_int32)), ("flags", C.c_uint32), ("b_layout", C.c_int32),
     ]
 
 
@@ -55,7 +61,7 @@ class _Info(C.Structure):
     _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64)] + [
         (n, C.c_int32) for n in ("BM", "BN", "swizzle", "wave_size", "NT", "T", "P", "num_units",
                                  "mode", "ranks", "dtype", "num_problems", "device", "clock_khz",
-                                 "sig_words", "flag_offset")]
+                                 "sig_words", "flag_offset", "stamp_offset", "flags")]
 
 
 _lib = None
@@ -82,6 +88,9 @@ def lib() -> C.CDLL:
             "fo_gemm_plain": [vp, vp, vp, vp, vp],
             "fo_gemm_signal_serialized": [vp, vp, vp, vp, vp, u32, vp, vp],
             "fo_consume_group": [vp, vp, vp, vp, vp, u32, i32, i32, vp, u64, i32, vp, vp],
+            "fo_consume_group_gated": [vp, vp, vp, vp, vp, u32, i32, i32, vp, vp, vp],
+            "fo_reorder_shards": [vp, vp, vp, vp],
+            "fo_row_exchange": [vp, vp, vp, vp, i32, vp],
             "fo_stream_create": [C.POINTER(vp)],
             "fo_stream_destroy": [vp],
             "fo_reorder_post": [vp, vp, vp, vp],
@@ -95,6 +104,8 @@ def lib() -> C.CDLL:
             f.restype = C.c_int
         L.fo_status_string.argtypes = [C.c_int]
         L.fo_status_string.restype = C.c_char_p
+        L.fo_arch_supported.argtypes = [C.c_char_p]
+        L.fo_arch_supported.restype = C.c_int
         _lib = L
     return _lib
 
@@ -143,6 +154,11 @@ def _stream(s) -> int:
     return int(s.cuda_stream)
 
 
+def arch_supported(arch: Optional[str]) -> bool:
+    """``fo_arch_supported``: can a device with this gcnArchName run the kernels (gfx950)."""
+    return bool(lib().fo_arch_supported(None if arch is None else arch.encode()))
+
+
 def stream_create():
     """A HIP stream with a hardware queue of its own (``fo_stream_create``), as a torch stream."""
     import torch
@@ -161,11 +177,15 @@ class Plan:
     ``m_per_problem``: rows of each problem (an int for a plain GEMM).
     ``composition``: waves per group (a partition of T); None = one wave per group.
     ``host_only``: build the tables without a GPU (the enqueue calls then refuse it).
+    ``epoch_stamps``: the stale-read detector (``FO_PLAN_EPOCH_STAMPS``): one stamp word per slot in
+    the signal buffer, written by the signaling GEMM and checked by the consumer.
+    ``b_layout``: "nk" (B stored [N, K], the only one implemented) or "kn" (refused).
     """
 
     def __init__(self, m_per_problem, N: int, K: int, dtype: str = "bf16", *, BM: int = 0, BN: int = 0,
                  swizzle: int = 0, wave_size: int = 0, composition: Optional[Sequence[int]] = None,
-                 mode: str = "tile", ranks: int = 1, row_dest=None, dispatch_order=None, host_only: bool = False):
+                 mode: str = "tile", ranks: int = 1, row_dest=None, dispatch_order=None, host_only: bool = False,
+                 epoch_stamps: bool = False, b_layout: str = "nk"):
         L = lib()
         if isinstance(m_per_problem, (int, np.integer)):
             m_per_problem = [int(m_per_problem)]
@@ -177,7 +197,8 @@ class Plan:
                   BM=int(BM), BN=int(BN), swizzle=int(swizzle), wave_size=int(wave_size),
                   num_groups=len(self._comp) if self._comp is not None else 0, waves_per_group=cp,
                   mode=_MODES[mode], ranks=int(ranks), row_dest=rp, dispatch_order=dp,
-                  flags=FO_PLAN_HOST_ONLY if host_only else 0)
+                  flags=(FO_PLAN_HOST_ONLY if host_only else 0) | (FO_PLAN_EPOCH_STAMPS if epoch_stamps else 0),
+                  b_layout=_B_LAYOUTS[b_layout])
         h = C.c_void_p()
         _check(L.fo_plan_groups(C.byref(d), C.byref(h)), "fo_plan_groups")
         self._h = h
@@ -186,7 +207,8 @@ class Plan:
         self.info = {n: getattr(info, n) for n, _ in _Info._fields_}
         self.dtype = dtype
         self.mode = mode
-        for k in ("M", "N", "K", "BM", "BN", "NT", "T", "P", "num_units", "sig_words", "flag_offset"):
+        for k in ("M", "N", "K", "BM", "BN", "NT", "T", "P", "num_units", "sig_words", "flag_offset",
+                  "stamp_offset"):
             setattr(self, k, self.info[k])
         self.W = self.info["wave_size"]
         self.S = self.info["swizzle"]
@@ -252,6 +274,12 @@ class Plan:
         """The flag words flag[P] of a signal buffer (a view)."""
         return sig[self.flag_offset:self.flag_offset + self.P]
 
+    def stamps_of(self, sig):
+        """The epoch stamps, one per slot, of a signal buffer (a view); plans with epoch_stamps only."""
+        if self.stamp_offset < 0:
+            raise ValueError("the plan has no epoch stamps")
+        return sig[self.stamp_offset:self.stamp_offset + self.NT]
+
     def gemm_signal(self, A, B, reorder_buf, sig, epoch: int, trace=None, stream=None):
         _check(lib().fo_gemm_signal(
             self._h, _ptr(A, numel=self.M * self.K, itemsize=2, name="A"),
@@ -286,6 +314,31 @@ class Plan:
             _ptr(sig, numel=self.sig_words, itemsize=4, name="sig"), int(epoch), int(g_begin), int(g_end),
             _ptr(status, numel=1, itemsize=4, name="status"), int(timeout_us), int(num_workgroups),
             _ptr(trace, numel=self.P, itemsize=8, name="trace"), _stream(stream)), "fo_consume_group")
+
+    def consume_group_gated(self, send, peer, recv, sig, epoch: int, status, g_begin: int = 0,
+                            g_end: Optional[int] = None, trace=None, stream=None):
+        """Consumer waiting in the stream's queue for each group's flag (``fo_consume_group_gated``)."""
+        g_end = self.P if g_end is None else g_end
+        _check(lib().fo_consume_group_gated(
+            self._h, _ptr(send, numel=self.mn, itemsize=2, name="send"),
+            _ptr(peer, numel=self.mn, itemsize=2, name="peer"), _ptr(recv, numel=self.mn, itemsize=2, name="recv"),
+            _ptr(sig, numel=self.sig_words, itemsize=4, name="sig"), int(epoch), int(g_begin), int(g_end),
+            _ptr(status, numel=1, itemsize=4, name="status"), _ptr(trace, numel=self.P, itemsize=8, name="trace"),
+            _stream(stream)), "fo_consume_group_gated")
+
+    def reorder_shards(self, reordered, gathered, stream=None):
+        """ReduceScatter plans: every rank's row shard, back to back (``fo_reorder_shards``)."""
+        _check(lib().fo_reorder_shards(self._h, _ptr(reordered, numel=self.mn, itemsize=2, name="reordered"),
+                                       _ptr(gathered, numel=self.mn, itemsize=2, name="gathered"),
+                                       _stream(stream)), "fo_reorder_shards")
+
+    def row_exchange(self, gathered, out, bias=None, act: str = "none", stream=None):
+        """Block-cyclic row exchange of the gathered shards into row-major ``out``, fused with bias and
+        activation (``fo_row_exchange``)."""
+        _check(lib().fo_row_exchange(self._h, _ptr(gathered, numel=self.mn, itemsize=2, name="gathered"),
+                                     _ptr(out, numel=self.mn, itemsize=2, name="out"),
+                                     _ptr(bias, numel=self.num_problems * self.N, itemsize=2, name="bias"),
+                                     _ACTS[act], _stream(stream)), "fo_row_exchange")
 
     def reorder_post(self, reordered, out, stream=None, groups: Optional[tuple] = None):
         """Inverse mapping into row-major ``out``; ``groups=(g_begin, g_end)`` restricts it to the

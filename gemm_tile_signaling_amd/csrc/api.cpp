@@ -72,13 +72,54 @@ int fo_consume_group(const fo_plan *p, const void *send, const void *peer, void 
   if (!buf_ok(p, send) || !buf_ok(p, peer) || !buf_ok(p, recv)) return FO_ERR_INVALID;
   if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return FO_ERR_INVALID;
   if (!dev_status || (reinterpret_cast<uintptr_t>(dev_status) & 3u)) return FO_ERR_INVALID;
-  if (num_workgroups < 0 || num_workgroups > 65536) return FO_ERR_INVALID;
-  const int32_t grid = num_workgroups ? num_workgroups : (p->num_cus > 0 ? p->num_cus : 256);
+  // at most one persistent consumer workgroup per CU, so that the GEMM's workgroups still fit beside them
+  if (num_workgroups < 0 || num_workgroups > p->num_cus) return FO_ERR_INVALID;
+  const int32_t grid = num_workgroups ? num_workgroups : p->num_cus;
   const uint64_t us = timeout_us ? timeout_us : 2000000ull;
   if (us > (1ull << 40)) return FO_ERR_INVALID;
   if (trace && (reinterpret_cast<uintptr_t>(trace) & 7u)) return FO_ERR_INVALID;
   return fo::launch_consume(p, send, peer, recv, sig, epoch, g_begin, g_end, dev_status, us * p->ticks_per_us, grid,
                             trace, stream);
+}
+
+int fo_consume_group_gated(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
+                           uint32_t epoch, int32_t g_begin, int32_t g_end, int32_t *dev_status, uint64_t *trace,
+                           hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (g_begin < 0 || g_end > p->P || g_begin > g_end) return FO_ERR_INVALID;
+  if (g_begin == g_end) return FO_OK;
+  if (!buf_ok(p, send) || !buf_ok(p, peer) || !buf_ok(p, recv)) return FO_ERR_INVALID;
+  if (!sig || (reinterpret_cast<uintptr_t>(sig) & 3u) || epoch == 0) return FO_ERR_INVALID;
+  if (!dev_status || (reinterpret_cast<uintptr_t>(dev_status) & 3u)) return FO_ERR_INVALID;
+  if (trace && (reinterpret_cast<uintptr_t>(trace) & 7u)) return FO_ERR_INVALID;
+  if (!p->can_wait_value) return FO_ERR_UNSUPPORTED;
+  const uint32_t *flag = sig + p->flag_offset();
+  for (int32_t g = g_begin; g < g_end; ++g) {
+    // the stream's queue waits until flag[g] >= epoch, then runs the group's kernel
+    if (hipStreamWaitValue32(stream, const_cast<uint32_t *>(flag + g), epoch, hipStreamWaitValueGte, 0xFFFFFFFFu) !=
+        hipSuccess)
+      return FO_ERR_HIP;
+    const int rc = fo::launch_consume_ready(p, send, peer, recv, sig, epoch, g, dev_status, trace, stream);
+    if (rc != FO_OK) return rc;
+  }
+  return FO_OK;
+}
+
+int fo_reorder_shards(const fo_plan *p, const void *reordered, void *gathered, hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (p->mode != FO_MODE_SUBTILE) return FO_ERR_INVALID;
+  if (!buf_ok(p, reordered) || !buf_ok(p, gathered)) return FO_ERR_INVALID;
+  return fo::launch_shards(p, reordered, gathered, stream);
+}
+
+int fo_row_exchange(const fo_plan *p, const void *gathered, void *out, const void *bias, int32_t act,
+                    hipStream_t stream) {
+  if (!device_ready(p)) return FO_ERR_INVALID;
+  if (p->mode != FO_MODE_SUBTILE) return FO_ERR_INVALID;
+  if (!buf_ok(p, gathered) || !buf_ok(p, out)) return FO_ERR_INVALID;
+  if (bias && !aligned16(bias)) return FO_ERR_INVALID;
+  if (act != FO_ACT_NONE && act != FO_ACT_RELU && act != FO_ACT_SILU) return FO_ERR_INVALID;
+  return fo::launch_row_exchange(p, gathered, out, bias, act, stream);
 }
 
 int fo_reorder_post(const fo_plan *p, const void *reordered, void *out, hipStream_t stream) {

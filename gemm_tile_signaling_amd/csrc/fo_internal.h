@@ -68,7 +68,9 @@ struct fo_plan {
   int32_t NT = 0, T = 0, P = 0;
   int32_t mode = 0, ranks = 1, dtype = 0, num_problems = 1;
   int32_t band_rows = 0;
+  uint32_t flags = 0;             // FO_PLAN_* bits
   bool host_only = false;
+  bool can_wait_value = false;    // the device's queues can wait on a memory value
   int32_t device = -1;
   int32_t num_cus = 0;
   uint64_t ticks_per_us = 100;   // device wall clock rate
@@ -81,6 +83,8 @@ struct fo_plan {
   std::vector<fo::TileDesc> slots;       // NT
   std::vector<int64_t> dbase;            // NT * D (subtoken)
   std::vector<int32_t> row_dest, row_rank;  // M (subtoken)
+  std::vector<int32_t> group_first;      // P + 1: first slot of each group
+  std::vector<int32_t> problem_row0;     // num_problems + 1: first output row of each problem
 
   // device copies (one allocation)
   void *dev_block = nullptr;
@@ -91,11 +95,17 @@ struct fo_plan {
   const int64_t *d_dbase = nullptr;
   const int32_t *d_row_dest = nullptr;
   const int32_t *d_row_rank = nullptr;
+  const int32_t *d_group_first = nullptr;
+  const int32_t *d_problem_row0 = nullptr;
 
   // Signal words: cnt[P] at word 0, flag[P] from the next multiple of 64 words,
   // so the lines consumers poll are not the lines every tile's atomic updates.
+  // With FO_PLAN_EPOCH_STAMPS, one stamp word per slot follows, from the next
+  // multiple of 64 words after the flags.
   int32_t flag_offset() const { return (P + 63) / 64 * 64; }
-  int32_t sig_words() const { return flag_offset() + P; }
+  bool stamps() const { return (flags & FO_PLAN_EPOCH_STAMPS) != 0; }
+  int32_t stamp_offset() const { return stamps() ? flag_offset() + (P + 63) / 64 * 64 : -1; }
+  int32_t sig_words() const { return stamps() ? stamp_offset() + NT : flag_offset() + P; }
 
   fo::Layout layout(bool device_side) const {
     fo::Layout L{};
@@ -118,6 +128,12 @@ int launch_gemm(const fo_plan *p, const void *A, const void *B, void *C, bool ro
 int launch_consume(const fo_plan *p, const void *send, const void *peer, void *recv,
                    const uint32_t *sig, uint32_t epoch, int32_t g_begin, int32_t g_end,
                    int32_t *status, uint64_t timeout_ticks, int32_t grid, uint64_t *trace, hipStream_t s);
+// one group, launched after its signal: no polling, a grid sized to the span
+int launch_consume_ready(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
+                         uint32_t epoch, int32_t g, int32_t *status, uint64_t *trace, hipStream_t s);
+int launch_shards(const fo_plan *p, const void *src, void *gathered, hipStream_t s);
+int launch_row_exchange(const fo_plan *p, const void *gathered, void *out, const void *bias, int act,
+                        hipStream_t s);
 int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajor, int32_t slot_begin,
                    int32_t slot_end, hipStream_t s);
 int launch_post_ep(const fo_plan *p, const void *src, void *dst, const void *bias, int act, hipStream_t s);

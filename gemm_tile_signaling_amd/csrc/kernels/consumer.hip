@@ -27,8 +27,21 @@
 // resources, so the tail needs no branches: loads past the end read zeros and
 // stores past the end are dropped.  The kernel holds no LDS beyond one word
 // and few registers, so it can stay resident next to the GEMM's workgroups.
+//
+// The same kernel also runs as the second half of the gated consumer: the
+// stream's hardware queue waits for the group's flag (hipStreamWaitValue32)
+// and only then launches it over that one group, with a grid sized to the
+// span; its single check of the flag then passes at once.
+//
+// Epoch stamps (optional, a plan flag): after a group's wait every workgroup
+// reads its share of the group's per-slot stamps with the same device-coherent
+// loads it uses for the span; a stamp other than the current epoch means the
+// signal was seen before the tile it covers, and FO_ERR_STALE goes to the
+// status word.
 #include "../fo_internal.h"
 #include "buffer.h"
+
+#include <algorithm>
 
 namespace fo {
 namespace {
@@ -39,7 +52,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;          // 16-byte chunks in flight per thread
+constexpr int kUnrollPersistent = 8;  // 16-byte chunks in flight per thread, persistent grid
+constexpr int kUnrollReady = 4;       // the same, grid sized to the span (gated launch)
 constexpr int kNT = 2;              // buffer cache policy: nontemporal (each byte is streamed once)
 constexpr int kCoherent = 16;       // buffer cache policy: device-coherent load
 
@@ -50,6 +64,8 @@ struct ConsumeParams {
   const uint32_t *flag;
   const int64_t *unit_off;
   const int32_t *group_unit;
+  const int32_t *group_first;  // first slot of each group (P + 1)
+  const uint32_t *stamps;      // NULL, or one epoch stamp per slot
   int32_t *status;
   uint64_t *trace;         // NULL or [P]: wall clock when workgroup 0's wait for a group ended
   uint64_t timeout_ticks;
@@ -75,7 +91,13 @@ __device__ __forceinline__ u32x4 add8<_Float16>(u32x4 a, u32x4 b) {
 // flag values only grow, one step per launch; compare as a signed distance
 __device__ __forceinline__ bool reached(uint32_t v, uint32_t epoch) { return (int32_t)(v - epoch) >= 0; }
 
-template <typename T>
+__device__ __forceinline__ void record_status(int32_t *status, int code) {
+  int expected = 0;
+  __hip_atomic_compare_exchange_strong(status, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int UNROLL>
 __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
   __shared__ int s_go;
   const int tid = threadIdx.x;
@@ -93,9 +115,7 @@ __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
             break;
           }
           if (wall_clock64() - t0 > p.timeout_ticks) {
-            int expected = 0;
-            __hip_atomic_compare_exchange_strong(p.status, &expected, (int)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            record_status(p.status, FO_ERR_TIMEOUT);
             go = 0;
             break;
           }
@@ -110,6 +130,14 @@ __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
     if (!go) return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no span load is hoisted above the wait
 
+    if (p.stamps) {  // every tile of the group carries this epoch's stamp
+      const int32_t s0 = p.group_first[g], s1 = p.group_first[g + 1];
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.stamps + s0, (uint32_t)(s1 - s0) * 4u);
+      for (int32_t i = blockIdx.x * kThreads + tid; i < s1 - s0; i += stride)
+        if (__builtin_amdgcn_raw_buffer_load_b32(rt, (uint32_t)i * 4u, 0, kCoherent | kNT) != p.epoch)
+          record_status(p.status, FO_ERR_STALE);
+    }
+
     // The group's units tile its span back to back, and every unit gets the
     // same elementwise reduction, so the span is streamed as one range.
     const int64_t lo = p.unit_off[p.group_unit[g]], hi = p.unit_off[p.group_unit[g + 1]];  // multiples of 8
@@ -118,19 +146,40 @@ __global__ __launch_bounds__(kThreads) void consume_kernel(ConsumeParams p) {
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.peer + lo, bytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.recv + lo, bytes);
     const uint32_t n = bytes >> 4;  // 16-byte chunks in the span
-    for (uint32_t c0 = blockIdx.x * kThreads + tid; c0 < n; c0 += kUnroll * stride) {
-      u32x4 a[kUnroll], b[kUnroll];
+    for (uint32_t c0 = blockIdx.x * kThreads + tid; c0 < n; c0 += UNROLL * stride) {
+      u32x4 a[UNROLL], b[UNROLL];
 #pragma unroll
-      for (int i = 0; i < kUnroll; ++i) {
+      for (int i = 0; i < UNROLL; ++i) {
         const uint32_t off = (c0 + i * stride) * 16u;
         a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent | kNT);
         b[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kNT);
       }
 #pragma unroll
-      for (int i = 0; i < kUnroll; ++i)
+      for (int i = 0; i < UNROLL; ++i)
         __builtin_amdgcn_raw_buffer_store_b128(add8<T>(a[i], b[i]), rr, (c0 + i * stride) * 16u, 0, kNT);
     }
   }
+}
+
+ConsumeParams params(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
+                     uint32_t epoch, int32_t g_begin, int32_t g_end, int32_t *status, uint64_t timeout_ticks,
+                     uint64_t *trace) {
+  ConsumeParams cp{};
+  cp.send = static_cast<const uint16_t *>(send);
+  cp.peer = static_cast<const uint16_t *>(peer);
+  cp.recv = static_cast<uint16_t *>(recv);
+  cp.flag = sig + p->flag_offset();
+  cp.unit_off = p->d_unit_off;
+  cp.group_unit = p->d_group_unit;
+  cp.group_first = p->d_group_first;
+  cp.stamps = p->stamps() ? sig + p->stamp_offset() : nullptr;
+  cp.status = status;
+  cp.trace = trace;
+  cp.timeout_ticks = timeout_ticks;
+  cp.epoch = epoch;
+  cp.g_begin = g_begin;
+  cp.g_end = g_end;
+  return cp;
 }
 
 }  // namespace
@@ -139,23 +188,26 @@ int launch_consume(const fo_plan *p, const void *send, const void *peer, void *r
                    uint32_t epoch, int32_t g_begin, int32_t g_end, int32_t *status, uint64_t timeout_ticks,
                    int32_t grid, uint64_t *trace, hipStream_t s) {
   if (g_begin >= g_end) return FO_OK;
-  ConsumeParams cp{};
-  cp.send = static_cast<const uint16_t *>(send);
-  cp.peer = static_cast<const uint16_t *>(peer);
-  cp.recv = static_cast<uint16_t *>(recv);
-  cp.flag = sig + p->flag_offset();
-  cp.unit_off = p->d_unit_off;
-  cp.group_unit = p->d_group_unit;
-  cp.status = status;
-  cp.trace = trace;
-  cp.timeout_ticks = timeout_ticks;
-  cp.epoch = epoch;
-  cp.g_begin = g_begin;
-  cp.g_end = g_end;
+  const ConsumeParams cp = params(p, send, peer, recv, sig, epoch, g_begin, g_end, status, timeout_ticks, trace);
   if (p->dtype == FO_BF16)
-    hipLaunchKernelGGL(consume_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, s, cp);
+    hipLaunchKernelGGL((consume_kernel<__bf16, kUnrollPersistent>), dim3(grid), dim3(kThreads), 0, s, cp);
   else
-    hipLaunchKernelGGL(consume_kernel<_Float16>, dim3(grid), dim3(kThreads), 0, s, cp);
+    hipLaunchKernelGGL((consume_kernel<_Float16, kUnrollPersistent>), dim3(grid), dim3(kThreads), 0, s, cp);
+  return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
+}
+
+int launch_consume_ready(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
+                         uint32_t epoch, int32_t g, int32_t *status, uint64_t *trace, hipStream_t s) {
+  // launched behind the queue's wait for the flag: the kernel's own wait passes at once
+  const ConsumeParams cp = params(p, send, peer, recv, sig, epoch, g, g + 1, status, 2000000ull * p->ticks_per_us,
+                                  trace);
+  const int64_t chunks = (p->unit_off[p->group_unit[g + 1]] - p->unit_off[p->group_unit[g]]) / 8;
+  const int64_t per_wg = (int64_t)kThreads * kUnrollReady;
+  const int32_t grid = (int32_t)std::min<int64_t>(std::max<int64_t>((chunks + per_wg - 1) / per_wg, 1), 16384);
+  if (p->dtype == FO_BF16)
+    hipLaunchKernelGGL((consume_kernel<__bf16, kUnrollReady>), dim3(grid), dim3(kThreads), 0, s, cp);
+  else
+    hipLaunchKernelGGL((consume_kernel<_Float16, kUnrollReady>), dim3(grid), dim3(kThreads), 0, s, cp);
   return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
 }
 

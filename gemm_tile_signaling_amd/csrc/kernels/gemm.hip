@@ -54,7 +54,9 @@
 //     a barrier, and one lane releases the tile to device scope and
 //     increments cnt[group]; the lane that brings it to epoch * |G_group|
 //     stores flag[group] = epoch with release semantics.  The signal's waits
-//     thus overlap the next tile's first loads.
+//     thus overlap the next tile's first loads.  With epoch stamps on, that
+//     lane also stores the epoch into the slot's stamp just before the
+//     release, so a consumer can check what the release made visible.
 //   * A third instantiation serializes the waves for tests and traces (a
 //     device-wide barrier and a snapshot of the signal words after every
 //     wave, cooperative launch); the hot path never runs it.
@@ -164,6 +166,7 @@ struct GemmParams {
   uint32_t *flag;
   const int32_t *thr;      // |G_j|
   uint64_t *trace;
+  uint32_t *stamps;        // NULL, or one word per slot: the epoch, once the slot's tile is stored
   uint32_t epoch;
   int32_t P;
   uint32_t *serial;        // serialized waves only: snapshots [T][2P], then barrier counter, then status
@@ -494,6 +497,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         wait_slices<C::LOADS, C::DIST>(nk);
       __syncthreads();
       if (tid == 0) {
+        // the stamp is released together with the tile's stores
+        if (p.stamps) __hip_atomic_store(&p.stamps[b], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(&p.cnt[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool fire = old + 1u == p.epoch * (uint32_t)p.thr[grp];
@@ -567,6 +572,7 @@ int launch_gemm(const fo_plan *p, const void *A, const void *B, void *Cout, bool
   gp.flag = sig ? sig + p->flag_offset() : nullptr;
   gp.thr = p->d_group_tiles;
   gp.trace = sig ? trace : nullptr;
+  gp.stamps = sig && p->stamps() ? sig + p->stamp_offset() : nullptr;
   gp.epoch = epoch;
   gp.P = p->P;
   gp.serial = serial;

@@ -23,6 +23,8 @@
 #include "../fo_internal.h"
 #include "buffer.h"
 
+#include <algorithm>
+
 namespace fo {
 namespace {
 
@@ -37,12 +39,26 @@ struct ReorderParams {
   const TileDesc *slots;
   Layout L;
   int64_t N;
+  // Row-major side of the move: row m at m * N, or, with shard_rows > 0, at
+  // shard_row(m) * N, the row's place in the gathered ReduceScatter shards.
+  int32_t shard_rows;    // M / R (0: plain row-major)
+  int32_t band_rows;     // BM / R
+  int32_t BM;
   uint32_t bytes;  // 2 * M * N, the size of both buffers
   int32_t to_rowmajor;
   const uint16_t *bias;  // epilogue only: [problems][N], or NULL
   uint32_t bias_bytes;
   int32_t slot0;         // first slot of the launch: workgroup (x, y) moves slot slot0 + x
 };
+
+// Rank k of R owns the rows whose band inside their tile row is k (rows m
+// with floor((m mod BM) / (BM/R)) == k), kept as a shard in increasing row
+// order; the shards lie back to back.  Row m's place among them.  Problems
+// start at multiples of BM, so m mod BM is the row inside its tile.
+__host__ __device__ __forceinline__ int64_t shard_row(int64_t m, int32_t BM, int32_t band, int32_t shard_rows) {
+  const int64_t r = m % BM;
+  return (r / band) * shard_rows + (m / BM) * band + r % band;
+}
 
 template <int RPB, int CPR>  // rows per block, 16-byte chunks per tile row
 __global__ __launch_bounds__(kThreads) void reorder_kernel(ReorderParams p) {
@@ -55,7 +71,9 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(ReorderParams p) {
   const int tid = threadIdx.x;
   if (tid < RPB && r0 + tid < t.rows) {
     const uint32_t reo = (uint32_t)row_offset(p.L, t, slot, r0 + tid) * 2u;
-    const uint32_t rm = (uint32_t)((int64_t)(t.row0 + r0 + tid) * p.N + t.col0) * 2u;
+    const int64_t m = t.row0 + r0 + tid;
+    const int64_t row = p.shard_rows ? shard_row(m, p.BM, p.band_rows, p.shard_rows) : m;
+    const uint32_t rm = (uint32_t)(row * p.N + t.col0) * 2u;
     src_row[tid] = p.to_rowmajor ? reo : rm;
     dst_row[tid] = p.to_rowmajor ? rm : reo;
   }
@@ -151,6 +169,70 @@ __global__ __launch_bounds__(kThreads) void post_ep_kernel(ReorderParams p) {
   }
 }
 
+// out row m = gathered row shard_row(m): the block-cyclic row exchange after
+// the AllGather of the ReduceScatter shards, with the element-wise epilogue.
+// Only M, BM and R are needed (no per-slot records).  Workgroup (x, y) moves
+// rows [x*RB, x*RB + RB) and the 16-byte column chunks y*256 + tid, y*256 +
+// tid + gridDim.y*256, ...; a thread keeps its RB loads in flight, then
+// stores.  Every row of a problem shares the problem's bias row: the problem
+// of a row is found among the problems' first rows (a wave-uniform search).
+constexpr int kRowsPerBlock = 8;
+
+struct ExchangeParams {
+  const uint16_t *src;
+  uint16_t *dst;
+  const uint16_t *bias;
+  const int32_t *problem_row0;  // num_problems + 1
+  int32_t num_problems;
+  int32_t M, BM, band, shard_rows;
+  int32_t cpr;                  // 16-byte chunks per row (N / 8)
+  uint32_t bytes, bias_bytes;
+  int64_t N;
+};
+
+template <typename T, int ACT, bool BIAS>
+__global__ __launch_bounds__(kThreads) void row_exchange_kernel(ExchangeParams p) {
+  const int tid = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.x * kRowsPerBlock;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.src, p.bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dst, p.bytes);
+  for (int32_t c8 = blockIdx.y * kThreads + tid; c8 - tid < p.cpr; c8 += gridDim.y * kThreads) {
+    const bool col_in = c8 < p.cpr;
+    u32x4 v[kRowsPerBlock];
+    uint32_t dst_off[kRowsPerBlock];
+    int32_t prob[kRowsPerBlock];
+#pragma unroll
+    for (int i = 0; i < kRowsPerBlock; ++i) {
+      const int64_t m = m0 + i;
+      const bool in = col_in && m < p.M;
+      const int64_t src_row = shard_row(m, p.BM, p.band, p.shard_rows);
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? (uint32_t)(src_row * p.N * 2 + (int64_t)c8 * 16) : kOutside, 0,
+                                                   kNT);
+      dst_off[i] = in ? (uint32_t)(m * p.N * 2 + (int64_t)c8 * 16) : kOutside;
+      int32_t e = 0;  // problem of row m: problem_row0[e] <= m < problem_row0[e + 1]
+      if (BIAS)
+        while (e + 1 < p.num_problems && p.problem_row0[e + 1] <= m) ++e;
+      prob[i] = e;
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerBlock; ++i) {
+      f32x8 x = Vec8<T>::widen(v[i]);
+      if (BIAS) {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias_bytes);
+        const uint32_t boff = col_in ? (uint32_t)((int64_t)prob[i] * p.N * 2 + (int64_t)c8 * 16) : kOutside;
+        x = x + Vec8<T>::widen(__builtin_amdgcn_raw_buffer_load_b128(rb, boff, 0, 0));
+      }
+      if (ACT != FO_ACT_NONE) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = act<ACT>(x[e]);
+      }
+      // without bias or activation the value is passed through untouched (no rounding step)
+      const u32x4 o = (BIAS || ACT != FO_ACT_NONE) ? Vec8<T>::narrow(x) : v[i];
+      __builtin_amdgcn_raw_buffer_store_b128(o, rd, dst_off[i], 0, kNT);
+    }
+  }
+}
+
 template <typename T, int ACT, bool BIAS>
 void launch_post_ep_typed(const fo_plan *p, const ReorderParams &rp, hipStream_t s) {
   if (p->BN == 128)
@@ -176,6 +258,36 @@ void launch_post_ep_act(const fo_plan *p, const ReorderParams &rp, int act, hipS
   }
 }
 
+int launch_reorder_params(const fo_plan *p, const ReorderParams &rp, int32_t nslots, hipStream_t s) {
+  if (p->BN == 128) {
+    constexpr int RPB = 128;
+    hipLaunchKernelGGL((reorder_kernel<RPB, 16>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
+  } else if (p->BN == 64) {
+    constexpr int RPB = 64;
+    hipLaunchKernelGGL((reorder_kernel<RPB, 8>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
+  } else {
+    return FO_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
+}
+
+template <typename T, int ACT>
+void launch_exchange_act(const ExchangeParams &ep, dim3 grid, hipStream_t s) {
+  if (ep.bias)
+    hipLaunchKernelGGL((row_exchange_kernel<T, ACT, true>), grid, dim3(kThreads), 0, s, ep);
+  else
+    hipLaunchKernelGGL((row_exchange_kernel<T, ACT, false>), grid, dim3(kThreads), 0, s, ep);
+}
+
+template <typename T>
+void launch_exchange_typed(const ExchangeParams &ep, int act, dim3 grid, hipStream_t s) {
+  switch (act) {
+    case FO_ACT_RELU: launch_exchange_act<T, FO_ACT_RELU>(ep, grid, s); break;
+    case FO_ACT_SILU: launch_exchange_act<T, FO_ACT_SILU>(ep, grid, s); break;
+    default: launch_exchange_act<T, FO_ACT_NONE>(ep, grid, s);
+  }
+}
+
 }  // namespace
 
 int launch_post_ep(const fo_plan *p, const void *src, void *dst, const void *bias, int act, hipStream_t s) {
@@ -198,6 +310,49 @@ int launch_post_ep(const fo_plan *p, const void *src, void *dst, const void *bia
   return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
 }
 
+int launch_row_exchange(const fo_plan *p, const void *gathered, void *out, const void *bias, int act,
+                        hipStream_t s) {
+  if (p->M == 0) return FO_OK;
+  ExchangeParams ep{};
+  ep.src = static_cast<const uint16_t *>(gathered);
+  ep.dst = static_cast<uint16_t *>(out);
+  ep.bias = static_cast<const uint16_t *>(bias);
+  ep.problem_row0 = p->d_problem_row0;
+  ep.num_problems = p->num_problems;
+  ep.M = (int32_t)p->M;
+  ep.BM = p->BM;
+  ep.band = p->band_rows;
+  ep.shard_rows = (int32_t)(p->M / p->ranks);
+  ep.cpr = (int32_t)(p->N / 8);
+  ep.bytes = (uint32_t)(2 * p->M * p->N);
+  ep.bias_bytes = (uint32_t)(2 * (int64_t)p->num_problems * p->N);
+  ep.N = p->N;
+  const int64_t col_blocks = (ep.cpr + kThreads - 1) / kThreads;
+  const dim3 grid((uint32_t)((p->M + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)std::min<int64_t>(col_blocks, 1024));
+  if (p->dtype == FO_BF16)
+    launch_exchange_typed<__bf16>(ep, act, grid, s);
+  else
+    launch_exchange_typed<_Float16>(ep, act, grid, s);
+  return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
+}
+
+int launch_shards(const fo_plan *p, const void *src, void *gathered, hipStream_t s) {
+  if (p->NT == 0) return FO_OK;
+  ReorderParams rp{};
+  rp.src = static_cast<const uint16_t *>(src);
+  rp.dst = static_cast<uint16_t *>(gathered);
+  rp.slots = p->d_slots;
+  rp.L = p->layout(true);
+  rp.N = p->N;
+  rp.bytes = (uint32_t)(2 * p->M * p->N);
+  rp.to_rowmajor = 1;
+  rp.shard_rows = (int32_t)(p->M / p->ranks);
+  rp.band_rows = p->band_rows;
+  rp.BM = p->BM;
+  rp.slot0 = 0;
+  return launch_reorder_params(p, rp, p->NT, s);
+}
+
 int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajor, int32_t slot_begin,
                    int32_t slot_end, hipStream_t s) {
   const int32_t nslots = slot_end - slot_begin;
@@ -211,16 +366,7 @@ int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajo
   rp.bytes = (uint32_t)(2 * p->M * p->N);
   rp.to_rowmajor = to_rowmajor ? 1 : 0;
   rp.slot0 = slot_begin;
-  if (p->BN == 128) {
-    constexpr int RPB = 128;
-    hipLaunchKernelGGL((reorder_kernel<RPB, 16>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
-  } else if (p->BN == 64) {
-    constexpr int RPB = 64;
-    hipLaunchKernelGGL((reorder_kernel<RPB, 8>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
-  } else {
-    return FO_ERR_UNSUPPORTED;
-  }
-  return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
+  return launch_reorder_params(p, rp, nslots, s);
 }
 
 }  // namespace fo

@@ -36,7 +36,9 @@ void swizzle(int32_t tm_n, int32_t tn_n, int32_t S, int32_t first, std::vector<i
 }
 
 int upload(fo_plan *p) {
-  // one device block: slots, group_tiles, unit_off, group_unit, dbase, row_dest, row_rank
+  // one device block: slots, group_tiles, unit_off, group_unit, dbase, row_dest, row_rank,
+  // group_first, problem_row0
+  constexpr int kTables = 9;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t n_slots = p->slots.size() * sizeof(fo::TileDesc);
   const size_t n_gt = p->group_tiles.size() * sizeof(int32_t);
@@ -45,14 +47,22 @@ int upload(fo_plan *p) {
   const size_t n_db = p->dbase.size() * sizeof(int64_t);
   const size_t n_rd = p->row_dest.size() * sizeof(int32_t);
   const size_t n_rr = p->row_rank.size() * sizeof(int32_t);
-  size_t off[8];
+  const size_t n_gf = p->group_first.size() * sizeof(int32_t);
+  const size_t n_pr = p->problem_row0.size() * sizeof(int32_t);
+  size_t off[kTables];
   size_t total = 0;
-  const size_t sizes[7] = {n_slots, n_gt, n_uo, n_gu, n_db, n_rd, n_rr};
-  for (int i = 0; i < 7; ++i) { off[i] = total; total += align(sizes[i] ? sizes[i] : 1); }
+  const size_t sizes[kTables] = {n_slots, n_gt, n_uo, n_gu, n_db, n_rd, n_rr, n_gf, n_pr};
+  for (int i = 0; i < kTables; ++i) { off[i] = total; total += align(sizes[i] ? sizes[i] : 1); }
   if (hipGetDevice(&p->device) != hipSuccess) return FO_ERR_HIP;
-  int cus = 0, clk_khz = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, p->device) != hipSuccess) return FO_ERR_HIP;
+  if (!fo_arch_supported(prop.gcnArchName)) return FO_ERR_UNSUPPORTED;
+  int cus = 0, clk_khz = 0, wait_value = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess) return FO_ERR_HIP;
   if (hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, p->device) != hipSuccess) return FO_ERR_HIP;
+  if (hipDeviceGetAttribute(&wait_value, hipDeviceAttributeCanUseStreamWaitValue, p->device) != hipSuccess)
+    wait_value = 0;
+  p->can_wait_value = wait_value != 0;
   p->num_cus = cus;
   p->ticks_per_us = clk_khz > 0 ? (uint64_t)clk_khz / 1000u : 100u;
   if (p->ticks_per_us == 0) p->ticks_per_us = 1;
@@ -60,9 +70,10 @@ int upload(fo_plan *p) {
   if (hipMalloc(&blk, total) != hipSuccess) return FO_ERR_NOMEM;
   p->dev_block = blk;
   char *base = static_cast<char *>(blk);
-  const void *src[7] = {p->slots.data(), p->group_tiles.data(), p->unit_off.data(), p->group_unit.data(),
-                        p->dbase.data(), p->row_dest.data(), p->row_rank.data()};
-  for (int i = 0; i < 7; ++i)
+  const void *src[kTables] = {p->slots.data(),    p->group_tiles.data(), p->unit_off.data(),
+                              p->group_unit.data(), p->dbase.data(),   p->row_dest.data(),
+                              p->row_rank.data(),   p->group_first.data(), p->problem_row0.data()};
+  for (int i = 0; i < kTables; ++i)
     if (sizes[i] && hipMemcpy(base + off[i], src[i], sizes[i], hipMemcpyHostToDevice) != hipSuccess)
       return FO_ERR_HIP;
   p->d_slots = reinterpret_cast<const fo::TileDesc *>(base + off[0]);
@@ -72,6 +83,8 @@ int upload(fo_plan *p) {
   p->d_dbase = n_db ? reinterpret_cast<const int64_t *>(base + off[4]) : nullptr;
   p->d_row_dest = n_rd ? reinterpret_cast<const int32_t *>(base + off[5]) : nullptr;
   p->d_row_rank = n_rr ? reinterpret_cast<const int32_t *>(base + off[6]) : nullptr;
+  p->d_group_first = reinterpret_cast<const int32_t *>(base + off[7]);
+  p->d_problem_row0 = reinterpret_cast<const int32_t *>(base + off[8]);
   return FO_OK;
 }
 
@@ -81,14 +94,21 @@ int build(const fo_plan_desc *d, fo_plan *p) {
   if (d->N > INT32_MAX || d->K > INT32_MAX) return FO_ERR_INVALID;
   if (d->K % 64 != 0) return FO_ERR_UNSUPPORTED;
   if (d->dtype != FO_BF16 && d->dtype != FO_FP16) return FO_ERR_UNSUPPORTED;
+  if (d->b_layout == FO_B_KN) return FO_ERR_UNSUPPORTED;
+  if (d->b_layout != FO_B_NK) return FO_ERR_INVALID;
   if (d->mode < FO_MODE_TILE || d->mode > FO_MODE_SUBTOKEN) return FO_ERR_INVALID;
+  if (d->flags & ~(FO_PLAN_HOST_ONLY | FO_PLAN_EPOCH_STAMPS)) return FO_ERR_INVALID;
   p->desc = *d;
+  p->flags = d->flags;
   p->host_only = (d->flags & FO_PLAN_HOST_ONLY) != 0;
   p->N = d->N;
   p->K = d->K;
   p->BM = d->BM ? d->BM : 256;
   p->BN = d->BN ? d->BN : 128;
   if ((d->BM == 0) != (d->BN == 0) || !valid_tile(p->BM, p->BN)) return FO_ERR_UNSUPPORTED;
+  // The GEMM addresses a tile's A and B rows with 32-bit byte offsets from the
+  // tile's first row: every offset stays below max(BM, BN) * K * 2.
+  if ((int64_t)std::max(p->BM, p->BN) * p->K * 2 > (int64_t)UINT32_MAX) return FO_ERR_UNSUPPORTED;
   p->S = d->swizzle ? d->swizzle : 4;
   if (p->S < 1) return FO_ERR_INVALID;
   p->mode = d->mode;
@@ -198,6 +218,9 @@ int build(const fo_plan_desc *d, fo_plan *p) {
   }
   std::vector<int32_t> first_slot(p->P + 1, p->NT);
   for (int32_t s = p->NT - 1; s >= 0; --s) first_slot[p->group_of_slot[s]] = s;
+  p->group_first = first_slot;
+  p->problem_row0.assign(1, 0);
+  for (int64_t m : p->m_per_problem) p->problem_row0.push_back(p->problem_row0.back() + (int32_t)m);
 
   // per-slot records and spans
   p->slots.resize(p->NT);
@@ -328,7 +351,19 @@ int fo_plan_info_get(const fo_plan *p, fo_plan_info *o) {
   o->clock_khz = p->host_only ? 0 : (int32_t)(p->ticks_per_us * 1000u);
   o->sig_words = p->sig_words();
   o->flag_offset = p->flag_offset();
+  o->stamp_offset = p->stamp_offset();
+  o->flags = (int32_t)p->flags;
   return FO_OK;
+}
+
+int fo_arch_supported(const char *arch) {
+  if (!arch) return 0;
+  // the processor name ends at the first ':' (target features follow)
+  const char *want = "gfx950";
+  size_t i = 0;
+  for (; want[i]; ++i)
+    if (arch[i] != want[i]) return 0;
+  return arch[i] == '\0' || arch[i] == ':';
 }
 
 int fo_plan_tables(const fo_plan *p, int32_t *tile_of_slot, int32_t *slot_of_tile, int32_t *group_of_slot,
@@ -374,6 +409,7 @@ const char *fo_status_string(int code) {
     case FO_ERR_HIP: return "HIP runtime error";
     case FO_ERR_NOMEM: return "out of memory";
     case FO_ERR_TIMEOUT: return "consumer wait timed out";
+    case FO_ERR_STALE: return "consumer read a tile stamp of an older epoch after the signal";
     default: return "unknown status";
   }
 }

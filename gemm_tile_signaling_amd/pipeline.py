@@ -15,6 +15,13 @@ as the previous GEMM on its queue ends, but it touches its buffers only once
 a flag of its own epoch is raised, i.e. after this pass's GEMM has started,
 which is after the previous post-reorder (the last reader of recv) ended.
 
+Consumer: ``consumer="gated"`` (the default) enqueues, per group, a wait in
+the stream's hardware queue for the group's flag and then a streaming kernel
+over the span (``fo_consume_group_gated``): nothing occupies a CU until the
+group is signalled.  ``consumer="poll"`` runs the persistent consumer that
+polls the flags on the CUs (``fo_consume_group``), one workgroup per CU beside
+the GEMM.
+
 Streams: both come from ``fo_stream_create``, so each has a hardware queue of
 its own and the consumer really runs beside the GEMM.  Launch order: the GEMM
 is enqueued before its consumer and waits only for earlier passes' kernels,
@@ -36,10 +43,14 @@ from . import Plan, stream_create, stream_destroy
 
 class Pipeline:
     def __init__(self, plan: Plan, A, B, peer, *, consumer_workgroups: int = 0, timeout_us: int = 0,
-                 in_place: bool = False, post_per_group: bool = False, streams: Optional[tuple] = None):
+                 in_place: bool = False, post_per_group: bool = False, streams: Optional[tuple] = None,
+                 consumer: str = "gated"):
         import torch
         self.torch = torch
         self.plan = plan
+        if consumer not in ("gated", "poll"):
+            raise ValueError("consumer must be 'gated' or 'poll'")
+        self.consumer = consumer
         # post_per_group: the stream-B side runs consumer(g), post-reorder(g) for each group in turn,
         # so a group's tiles go back in place while later groups are computed
         self.post_per_group = post_per_group
@@ -120,9 +131,7 @@ class Pipeline:
         if self.post_per_group and p.P > 1:
             # events: 'consume' spans the whole stream-B side, 'post' the last group's post-reorder
             for g in range(p.P):
-                p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status, g_begin=g, g_end=g + 1,
-                                timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
-                                trace=consumer_trace, stream=s_comm)
+                self._consume(e, g, g + 1, consumer_trace, s_comm)
                 if "post" in ev and g == p.P - 1:
                     ev["post"][0].record(s_comm)
                 p.reorder_post(self.recv, self.out, stream=s_comm, groups=(g, g + 1))
@@ -131,9 +140,7 @@ class Pipeline:
             if "post" in ev:
                 ev["post"][1].record(s_comm)
         else:
-            p.consume_group(self.buf, self.peer, self.recv, self.sig, e, self.status,
-                            timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
-                            trace=consumer_trace, stream=s_comm)
+            self._consume(e, 0, p.P, consumer_trace, s_comm)
             if "consume" in ev:
                 ev["consume"][1].record(s_comm)
             if "post" in ev:
@@ -143,6 +150,16 @@ class Pipeline:
                 ev["post"][1].record(s_comm)
         self.post_stream = s_comm
         return e
+
+    def _consume(self, epoch, g0, g1, consumer_trace, stream):
+        p = self.plan
+        if self.consumer == "gated":
+            p.consume_group_gated(self.buf, self.peer, self.recv, self.sig, epoch, self.status, g_begin=g0, g_end=g1,
+                                  trace=consumer_trace, stream=stream)
+        else:
+            p.consume_group(self.buf, self.peer, self.recv, self.sig, epoch, self.status, g_begin=g0, g_end=g1,
+                            timeout_us=self.timeout_us, num_workgroups=self.consumer_workgroups,
+                            trace=consumer_trace, stream=stream)
 
     def join(self):
         """Make the current stream wait for both streams."""

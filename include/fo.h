@@ -50,7 +50,9 @@ typedef enum fo_status {
   FO_ERR_UNSUPPORTED = -2,  /* valid request the library does not implement (e.g. K % 64 != 0)*/
   FO_ERR_HIP = -3,          /* a HIP runtime call failed                                       */
   FO_ERR_NOMEM = -4,        /* host or device allocation failed at plan creation               */
-  FO_ERR_TIMEOUT = -5       /* device-side: the consumer waited longer than its time limit     */
+  FO_ERR_TIMEOUT = -5,      /* device-side: the consumer waited longer than its time limit     */
+  FO_ERR_STALE = -6         /* device-side: with FO_PLAN_EPOCH_STAMPS, the consumer read a
+                               tile stamp of an older epoch after its group's signal          */
 } fo_status;
 
 typedef enum fo_dtype { FO_BF16 = 0, FO_FP16 = 1 } fo_dtype;
@@ -71,8 +73,25 @@ typedef enum fo_act {
   FO_ACT_SILU = 2,   /* x / (1 + exp(-x))    */
 } fo_act;
 
+/* Storage of B.  Only FO_B_NK is implemented: a plan asking for FO_B_KN is refused with
+ * FO_ERR_UNSUPPORTED (the kernels stage B rows of K contiguous elements). */
+typedef enum fo_b_layout {
+  FO_B_NK = 0,       /* B stored [N, K], K contiguous (a linear layer's weight); the default */
+  FO_B_KN = 1        /* B stored [K, N], N contiguous: not supported                         */
+} fo_b_layout;
+
 /* Plan flags. */
 #define FO_PLAN_HOST_ONLY 0x1u   /* build the tables on the host only; enqueue calls reject the plan */
+#define FO_PLAN_EPOCH_STAMPS 0x2u /* stale-read detector: the signal buffer grows by one word per
+                                    slot (stamp_offset, fo_plan_info); the signaling GEMM writes the
+                                    epoch into its tile's stamp after the tile's stores and before
+                                    the release that precedes the count, and the consumer, after a
+                                    group's signal, reads every stamp of the group with the same
+                                    loads it uses for the span: a stamp of an older epoch means the
+                                    signal did not make the tile's writes visible, and it stores
+                                    FO_ERR_STALE into its status word (it still finishes the
+                                    group).  The stamps rely on the same device-scope release as
+                                    the data, so they observe the protocol, not just the data   */
 
 /*
  * Problem description.  C[M, N] = A[M, K] . B^T where B is stored [N, K]
@@ -95,7 +114,9 @@ typedef enum fo_act {
 typedef struct fo_plan_desc {
   int32_t num_problems;            /* >= 1                                                    */
   const int64_t *m_per_problem;    /* host [num_problems]: rows of each problem (>= 0)        */
-  int64_t N, K;                    /* N % 8 == 0, K % 64 == 0, both > 0; M*N <= 2^30          */
+  int64_t N, K;                    /* N % 8 == 0, K % 64 == 0, both > 0; M*N <= 2^30; the
+                                      tile's operand rows fit 32-bit byte offsets:
+                                      max(BM, BN) * K * 2 < 2^32 (K < 2^23 at BM = 256)       */
   int32_t dtype;                   /* fo_dtype                                                */
   int32_t BM, BN;                  /* tile: 256x128, 128x128 or 64x64; 0,0 = 256x128          */
   int32_t swizzle;                 /* S >= 1; 0 = 4                                           */
@@ -107,6 +128,7 @@ typedef struct fo_plan_desc {
   const int32_t *row_dest;         /* host [M], SUBTOKEN only: destination rank of each row   */
   const int32_t *dispatch_order;   /* host [NT] or NULL: explicit b -> tile permutation       */
   uint32_t flags;                  /* FO_PLAN_* bits                                          */
+  int32_t b_layout;                /* fo_b_layout; FO_B_KN -> FO_ERR_UNSUPPORTED              */
 } fo_plan_desc;
 
 typedef struct fo_plan fo_plan;
@@ -121,21 +143,48 @@ typedef struct fo_plan_info {
   int32_t mode, ranks, dtype, num_problems;
   int32_t device;                  /* HIP device the tables live on; -1 if host-only          */
   int32_t clock_khz;               /* rate of the device wall clock used by the traces; 0 if host-only */
-  int32_t sig_words;               /* uint32 words of the signal buffer: flag_offset + P      */
+  int32_t sig_words;               /* uint32 words of the signal buffer: flag_offset + P, or
+                                      stamp_offset + NT with FO_PLAN_EPOCH_STAMPS             */
   int32_t flag_offset;             /* word index of flag[0]: P rounded up to a multiple of 64 */
+  int32_t stamp_offset;            /* word index of stamp[0] (slot order) with
+                                      FO_PLAN_EPOCH_STAMPS, else -1                           */
+  int32_t flags;                   /* the plan's FO_PLAN_* bits                               */
 } fo_plan_info;
 
 /*
- * Build a plan: tile grid, dispatch order, waves, groups, mapping table,
- * thresholds |G_j| (in tiles), span and unit offsets, and the per-slot
- * records the kernels read.  Unless FO_PLAN_HOST_ONLY is set the tables are
- * uploaded once to the current HIP device; they are immutable afterwards, so
- * a plan may be shared by streams and threads.  The plan must outlive all
- * work enqueued with it.  *out is set only on FO_OK.
+ * Build a plan (deep-dive 一、信号机制 › Wave Group 设计 and 实现方法: 组级 Tile
+ * 计数 for the waves, groups and thresholds; 二、重排机制 › 解决方案: 映射表重排
+ * and Figure 6 for the mapping table and the three span layouts; 三、Wave Group
+ * 划分设计空间 for the partition): tile grid, dispatch order, waves, groups,
+ * mapping table, thresholds |G_j| (in tiles), span and unit offsets, and the
+ * per-slot records the kernels read.
+ *
+ * Unless FO_PLAN_HOST_ONLY is set the tables are uploaded once to the current
+ * HIP device (one device allocation, owned by the plan, freed by
+ * fo_plan_destroy); they are immutable afterwards, so a plan may be shared by
+ * streams and threads.  The plan must outlive all work enqueued with it.
+ * *out is set only on FO_OK; desc and every host array it points to are
+ * copied, the caller keeps them.
+ *
+ * Errors: FO_ERR_INVALID for a malformed description (null or negative
+ * sizes, a composition that does not sum to T, an entry < 1, a row_dest out
+ * of range, ReduceScatter with BM % R != 0 or a ragged tile, a dispatch order
+ * that is not a permutation); FO_ERR_UNSUPPORTED for a request the kernels do
+ * not implement: another tile shape, K % 64 != 0, an element type other than
+ * bf16/fp16, B stored [K, N], M*N > 2^30, max(BM, BN) * K * 2 >= 2^32, or a
+ * current device that is not gfx950 (fo_arch_supported); FO_ERR_HIP when the
+ * runtime cannot be queried; FO_ERR_NOMEM when an allocation fails.
  */
 int fo_plan_groups(const fo_plan_desc *desc, fo_plan **out);
 int fo_plan_destroy(fo_plan *plan);
 int fo_plan_info_get(const fo_plan *plan, fo_plan_info *out);
+
+/*
+ * 1 if a device whose gcnArchName is `arch` (e.g. "gfx950:sramecc+:xnack-")
+ * can run the kernels, i.e. its processor is gfx950; 0 otherwise or for NULL.
+ * fo_plan_groups applies it to the current device of a non-host-only plan.
+ */
+int fo_arch_supported(const char *arch);
 
 /*
  * Copy the plan's host tables into caller arrays (any may be NULL):
@@ -169,10 +218,9 @@ int fo_plan_offsets(const fo_plan *plan, int64_t *off);
  * Algorithm 1).  Scores every composition of the plan's T waves -- 2^(T-1)
  * candidates; the plan's own composition is not used -- with the pages'
  * latency model and returns the best:
- *   for each group i in order:
- *     t_acc_m = max(t_acc_p, t_acc_m) + lat(bytes of group i-1)   (0 for i = 0)
- *     t_acc_p = t_acc_p + gemm_seconds / T * (waves of group i)
- *   prediction = max(t_acc_p, t_acc_m) + lat(bytes of the last group)
+ *   compute_end(i) = gemm_seconds / T * (waves of groups 0 .. i)
+ *   comm_end(i)    = max(compute_end(i), comm_end(i-1)) + lat(bytes of group i),  comm_end(-1) = 0
+ *   prediction     = comm_end(P-1)
  * bytes of a group = its span (elements x 2).  lat() interpolates the
  * sampled curve (curve_bytes[points] > 0, strictly increasing;
  * curve_seconds[points] >= 0) linearly, holds the first sample's latency
@@ -201,7 +249,9 @@ int fo_plan_search(const fo_plan *plan, double gemm_seconds, const double *curve
  *      word 0 and the flags flag[P] at word flag_offset, the first multiple of
  *      64 words (256 bytes) at or after P, so that with a 256-byte aligned sig
  *      the flags that consumers poll never share a cache line with the
- *      counters every tile increments.  Zero it once before the first epoch.  Epochs start at 1 and increase by 1 per launch on
+ *      counters every tile increments.  With FO_PLAN_EPOCH_STAMPS the words
+ *      from stamp_offset hold one stamp per slot, which the launch sets to
+ *      epoch once the slot's tile is stored.  Zero it once before the first epoch.  Epochs start at 1 and increase by 1 per launch on
  *      the same sig, so no reset is needed between launches; after epoch e,
  *      cnt[j] == e*|G_j|.  epoch * max|G_j| must fit in 32 bits.
  * trace: NULL, or device uint64[2*NT + P]: for slot s, trace[2s] = wall
@@ -246,7 +296,16 @@ int fo_gemm_plain(const fo_plan *plan, const void *A, const void *B, void *C, hi
  * collective call on the contiguous span (deep-dive 二 › (1) code box;
  * 五 › 专用监控内核).
  *
- * num_workgroups: persistent grid size (0 = the device's CU count).
+ * num_workgroups: persistent grid size, 0 = the device's CU count; at most
+ *      the CU count, else FO_ERR_INVALID.  Residency: the consumer's
+ *      workgroups wait on the CUs for flags that the GEMM raises, so the GEMM's
+ *      W workgroups must still find room beside them.  A GEMM workgroup holds
+ *      up to 376 of a SIMD's 512 registers per lane and 144 KiB of the CU's
+ *      160 KiB LDS; a consumer workgroup is one wave per SIMD of at most 96
+ *      registers and no LDS to speak of, so one consumer workgroup per CU fits
+ *      beside the GEMM and two do not: a grid above the CU count could keep
+ *      GEMM workgroups from being dispatched until the consumer times out.
+ *      fo_consume_group_gated has no such condition.
  * timeout_us: upper bound on any one wait (0 = 2 s).  A workgroup that
  *      waits longer stores FO_ERR_TIMEOUT into *dev_status (if it was still
  *      0) and every workgroup then stops; later spans are left untouched.
@@ -264,7 +323,39 @@ int fo_consume_group(const fo_plan *plan, const void *send, const void *peer, vo
                      int32_t *dev_status, uint64_t timeout_us, int32_t num_workgroups,
                      uint64_t *trace, hipStream_t stream);
 
-/* Post-communication reordering: out[m*N + n] = reordered[off(m, n)] (inverse mapping). */
+/*
+ * Consumer waiting in the command processor instead of on the CUs
+ * (deep-dive 五 › 专用监控内核: the signal may reach the transfer stream as an
+ * event-like notification rather than through a polling kernel).  For g =
+ * g_begin .. g_end-1 in order it enqueues on `stream` a wait until flag[g] >=
+ * epoch (hipStreamWaitValue32, evaluated by the stream's hardware queue) and
+ * then a streaming kernel over g's span with the same arithmetic as
+ * fo_consume_group:  recv[u] = round(float(send[u]) + float(peer[u])).  The
+ * kernel is launched only once the group is signalled, so it never occupies a
+ * CU while it waits, and its grid is sized to the span (several workgroups
+ * per CU) instead of being persistent.
+ * The wait has no time limit: the signaling GEMM of `epoch` on the same sig
+ * must be enqueued (on another stream) or the stream never proceeds.
+ * dev_status: device int32 as for fo_consume_group; receives FO_ERR_STALE
+ * from the epoch-stamp check.  trace: NULL, or device uint64[P]: the wall
+ * clock when group g's kernel started streaming (workgroup 0), as for
+ * fo_consume_group.  FO_ERR_UNSUPPORTED if the device cannot wait on a value
+ * (hipDeviceAttributeCanUseStreamWaitValue).  Other arguments and errors as
+ * for fo_consume_group.
+ */
+int fo_consume_group_gated(const fo_plan *plan, const void *send, const void *peer, void *recv,
+                           const uint32_t *sig, uint32_t epoch, int32_t g_begin, int32_t g_end,
+                           int32_t *dev_status, uint64_t *trace, hipStream_t stream);
+
+/*
+ * Post-communication reordering (deep-dive 二、重排机制 › 解决方案: 映射表重排 --
+ * the inverse mapping puts each tile back where the GEMM would have stored it;
+ * Figure 6 for the three layouts; summary, Figure 5):
+ *   out[m*N + n] = reordered[off(m, n)]
+ * off() is the plan's layout (fo_plan_offsets).  reordered and out: device,
+ * M*N elements, distinct.  Errors: FO_ERR_INVALID for a null or misaligned
+ * buffer or a plan without device tables on the current device.
+ */
 int fo_reorder_post(const fo_plan *plan, const void *reordered, void *out, hipStream_t stream);
 
 /*
@@ -294,8 +385,48 @@ int fo_reorder_post_groups(const fo_plan *plan, int32_t g_begin, int32_t g_end, 
 int fo_reorder_post_ep(const fo_plan *plan, const void *reordered, void *out, const void *bias, int32_t act,
                        hipStream_t stream);
 
-/* Pre-communication reordering as a separate pass: reordered[off(m, n)] = in[m*N + n]. */
+/*
+ * Pre-communication reordering as a separate pass (deep-dive 二 › 解决方案: the
+ * mapping table gathers the tiles of a group into consecutive addresses so
+ * that one collective call can take them; the signaling GEMM does the same in
+ * its epilogue):
+ *   reordered[off(m, n)] = in[m*N + n]
+ * in and reordered: device, M*N elements, distinct.  Errors as for
+ * fo_reorder_post.
+ */
 int fo_reorder_pre(const fo_plan *plan, const void *in, void *reordered, hipStream_t stream);
+
+/*
+ * ReduceScatter + AllGather, the first half (deep-dive 二 › 不同通信原语的重排模式,
+ * (2) ReduceScatter + AllGather: after the ReduceScatter every rank holds band
+ * k of every tile, and these k-th pieces form complete rows).  A SUBTILE plan
+ * only (FO_ERR_INVALID otherwise).  Rank k owns the rows whose band inside
+ * their tile row is k -- rows m with floor((m mod BM) / (BM/R)) == k, a
+ * block-cyclic deal of blocks of BM/R rows -- and keeps them as a row-major
+ * shard of M/R rows in increasing row order.  This call writes every rank's
+ * shard from its segments of the reordered buffer through the mapping table:
+ *   gathered[k*(M/R)*N + i*N + n] = reordered[off(m, n)]
+ * for the row m that is the i-th row of rank k.  With the R shards placed back
+ * to back, `gathered` is the buffer an AllGather of the shards produces.
+ * reordered and gathered: device, M*N elements, distinct.
+ */
+int fo_reorder_shards(const fo_plan *plan, const void *reordered, void *gathered, hipStream_t stream);
+
+/*
+ * ReduceScatter + AllGather, the second half (same passage: the row order
+ * after the AllGather is corrected by a local row exchange, a block-cyclic
+ * permutation that needs no mapping table and merges with the element-wise
+ * operations).  A SUBTILE plan only.  Row m of the output is row
+ * k*(M/R) + floor(m / BM)*(BM/R) + (m mod (BM/R)) of `gathered`, with
+ * k = floor((m mod BM) / (BM/R)); computed from M, BM and R alone.  With the
+ * element-wise epilogue of fo_reorder_post_ep:
+ *   out[m*N + n] = round(act(float(gathered[row(m)*N + n]) + float(bias[e(m)*N + n])))
+ * bias: NULL or num_problems * N elements; act: fo_act.  gathered and out:
+ * device, M*N elements, distinct.  fo_reorder_shards followed by this call
+ * gives what fo_reorder_post_ep gives on the same reordered buffer.
+ */
+int fo_row_exchange(const fo_plan *plan, const void *gathered, void *out, const void *bias, int32_t act,
+                    hipStream_t stream);
 
 /*
  * A stream for the GEMM or the consumer side: a HIP stream on the current

@@ -86,3 +86,63 @@ def test_signal_buffer_layout():
     assert (edge.P, edge.flag_offset, edge.sig_words) == (64, 64, 128)
     empty = P(0, 64, 64, BM=64, BN=64, swizzle=1, wave_size=4, composition=(), host_only=True)
     assert (empty.P, empty.flag_offset, empty.sig_words) == (0, 0, 0)
+
+
+def test_status_string_of_the_stale_read_code():
+    assert fo.FO_ERR_STALE == -6
+    assert "stamp" in fo.status_string(-6)
+
+
+def test_layout_of_b_and_operand_limits():
+    """Only B stored [N, K] is implemented; a tile's operand rows must fit 32-bit byte offsets."""
+    P = fo.Plan
+    assert _code(lambda: P(256, 256, 256, host_only=True, b_layout="kn")) == -2
+    # max(BM, BN) * K * 2 must stay below 2^32: K = 2^23 is refused at BM = 256, accepted at BM = BN = 64
+    assert _code(lambda: P(256, 128, 2 ** 23, host_only=True)) == -2
+    assert P(256, 128, 2 ** 23 - 64, host_only=True).K == 2 ** 23 - 64
+    assert P(64, 64, 2 ** 23, BM=64, BN=64, host_only=True).K == 2 ** 23
+    assert _code(lambda: P(64, 64, 2 ** 25, BM=64, BN=64, host_only=True)) == -2
+
+
+def test_unknown_plan_flags_are_refused():
+    L = fo.lib()
+    m = (ctypes.c_int64 * 1)(256)
+    d = fo._Desc(num_problems=1, m_per_problem=ctypes.cast(m, ctypes.POINTER(ctypes.c_int64)), N=256, K=256,
+                 flags=fo.FO_PLAN_HOST_ONLY | 0x100)
+    h = ctypes.c_void_p()
+    assert L.fo_plan_groups(ctypes.byref(d), ctypes.byref(h)) == -1
+    d.flags = fo.FO_PLAN_HOST_ONLY
+    d.b_layout = 7
+    assert L.fo_plan_groups(ctypes.byref(d), ctypes.byref(h)) == -1
+
+
+def test_architecture_check():
+    """The kernels are gfx950 code: the name up to the first ':' must be exactly gfx950."""
+    assert fo.arch_supported("gfx950")
+    assert fo.arch_supported("gfx950:sramecc+:xnack-")
+    for other in ("gfx942", "gfx942:sramecc+:xnack-", "gfx90a", "gfx9500", "gfx95", "", None):
+        assert not fo.arch_supported(other), other
+
+
+def test_epoch_stamp_layout():
+    """With epoch stamps the signal buffer gains one word per slot after the flags, on a 64-word boundary."""
+    P = fo.Plan
+    p = P(256, 256, 64, "fp16", BM=64, BN=64, swizzle=2, wave_size=4, composition=(1, 2, 1), host_only=True,
+          epoch_stamps=True)
+    assert (p.P, p.flag_offset, p.stamp_offset, p.NT, p.sig_words) == (3, 64, 128, 16, 144)
+    assert p.info["flags"] == fo.FO_PLAN_HOST_ONLY | fo.FO_PLAN_EPOCH_STAMPS
+    many = P(64 * 80, 64, 64, BM=64, BN=64, swizzle=1, wave_size=1, host_only=True, epoch_stamps=True)
+    assert (many.flag_offset, many.stamp_offset, many.sig_words) == (128, 256, 256 + 80)
+    plain = P(256, 256, 64, "fp16", BM=64, BN=64, swizzle=2, wave_size=4, composition=(1, 2, 1), host_only=True)
+    assert plain.stamp_offset == -1
+    with pytest.raises(ValueError):
+        plain.stamps_of(np.zeros(plain.sig_words, np.int32))
+
+
+def test_new_enqueue_calls_reject_host_only_and_wrong_layouts():
+    p = fo.Plan(256, 256, 256, "fp16", BM=64, BN=64, swizzle=2, wave_size=4, mode="subtile", ranks=4,
+                host_only=True)
+    assert _code(lambda: p.consume_group_gated(16, 16, 16, 16, 1, 16, stream=0)) == -1
+    assert _code(lambda: p.consume_group_gated(16, 16, 16, 16, 1, 16, trace=20, stream=0)) == -1
+    assert _code(lambda: p.reorder_shards(16, 16, stream=0)) == -1
+    assert _code(lambda: p.row_exchange(16, 16, stream=0)) == -1

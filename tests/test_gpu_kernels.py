@@ -389,3 +389,94 @@ def test_every_kernel_with_buffers_above_bit31_of_the_low_word():
     tol_check_out(to_host(out).reshape(o.M, o.N), oracle.decode_bits(r["out"], dt), r["C64"], dt, "out")
     assert np.array_equal(to_host(Y), oracle.pre_reorder(Xh.reshape(o.M, o.N), r["off"]))
     del big
+
+
+# --------------------------------------------------------------------------- gated consumer
+
+@pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
+def test_consumer_gated_bit_exact(entry):
+    """The consumer whose stream's queue waits for each flag: bit-exact against the oracle over all groups,
+    and over a range of groups (the rest of recv untouched)."""
+    o, p = _plans(entry)
+    dt = entry[4]
+    send = random_bits(15, o.M * o.N, dt)
+    peer = random_bits(16, o.M * o.N, dt)
+    want = oracle.consume_add(send, peer, dt)
+    spans = group_spans(o)
+    say(f"consumer gated {entry[0]} P={o.P}")
+    sig = p.new_sig()
+    p.flag_of(sig).fill_(4)            # every group already signalled at epoch 4
+    status = zeros_i32(1)
+    dsend, dpeer = to_dev(send), to_dev(peer)
+    recv = empty16(o.M * o.N)
+    p.consume_group_gated(dsend, dpeer, recv, sig, 4, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(to_host(recv), want)
+    if o.P >= 2:
+        recv = empty16(o.M * o.N)
+        p.consume_group_gated(dsend, dpeer, recv, sig, 3, status, g_begin=1, g_end=o.P)   # flags >= 3 as well
+        torch.cuda.synchronize()
+        got = to_host(recv)
+        assert np.array_equal(got[spans[1]:], want[spans[1]:])
+        assert np.all(got[:spans[1]] == 0x7FC0)
+
+
+# --------------------------------------------------------------------------- ReduceScatter shards, row exchange
+
+SUBTILE = [e for e in PLANS if e[10] == "subtile"] + [
+    ("subtile_r8_multi", [256, 512], 256, 64, "bf16", 256, 128, 2, 3, None, "subtile", 8),
+    ("subtile_r16_64", [192], 128, 64, "fp16", 64, 64, 1, 5, None, "subtile", 16),
+]
+
+
+@pytest.mark.parametrize("entry", SUBTILE, ids=[e[0] for e in SUBTILE])
+def test_reorder_shards_and_row_exchange_bit_exact(entry):
+    from oracle.rowexchange import row_exchange, shard_reorder
+    o, p = _plans(entry)
+    dt = entry[4]
+    off = element_offsets(o)
+    Y = random_bits(17, o.M * o.N, dt)
+    want_g = shard_reorder(Y, off, o)
+    say(f"shards + row exchange {entry[0]} M={o.M} N={o.N} R={entry[11]}")
+    dY = to_dev(Y)
+    g, out = empty16(o.M * o.N), empty16(o.M * o.N)
+    p.reorder_shards(dY, g)
+    p.row_exchange(g, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(g), want_g)
+    assert np.array_equal(to_host(out), row_exchange(want_g, o).ravel())
+    assert np.array_equal(to_host(out), oracle.post_reorder(Y, off).ravel())
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "silu"])
+@pytest.mark.parametrize("entry", SUBTILE, ids=[e[0] for e in SUBTILE])
+def test_row_exchange_epilogue(entry, act):
+    """none / relu: bit-exact; silu within one unit in the last place (exp in fp32 against fp64)."""
+    from oracle.rowexchange import row_exchange_epilogue
+    o, p = _plans(entry)
+    dt = entry[4]
+    G = to_bits(draw(63, (o.M * o.N,), ("normal", 2.0)), dt)
+    bias = to_bits(draw(64, (len(o.m_per_problem) * o.N,), ("normal", 1.0)), dt)
+    dG = to_dev(G)
+    for b in (None, bias):
+        want = row_exchange_epilogue(G, o, dt, act, b, row_problems(o)).ravel()
+        say(f"row exchange epilogue {entry[0]} act={act} bias={b is not None}")
+        out = empty16(o.M * o.N)
+        p.row_exchange(dG, out, bias=to_dev(b) if b is not None else None, act=act)
+        torch.cuda.synchronize()
+        got = to_host(out)
+        if act == "silu":
+            assert ulp_distance(got, want).max() <= 1
+        else:
+            assert np.array_equal(got, want)
+
+
+def test_shard_calls_refuse_other_layouts():
+    entry = PLANS[1]
+    o, p = _plans(entry)
+    x = empty16(o.M * o.N)
+    for call in (lambda: p.reorder_shards(x, x), lambda: p.row_exchange(x, x)):
+        with pytest.raises(fo.FoError) as e:
+            call()
+        assert e.value.code == fo.FO_ERR_INVALID

@@ -1,10 +1,12 @@
 """The consumer runs beside the GEMM: device timestamps show causality and overlap.
 
 Both kernels stamp the device wall clock: the GEMM when each tile signals,
-the consumer when its wait for a group ends.  Causality (a group is consumed
-only after its last tile signalled) must hold for every group; overlap (the
-first group is consumed while the GEMM still computes the last group) shows
-that the two streams really run at the same time.
+the consumer when its wait for a group ends (the polling consumer) or when
+the group's kernel starts behind the queue's wait (the gated consumer).
+Causality (a group is consumed only after its last tile signalled) must hold
+for every group; overlap (the first group is consumed while the GEMM still
+computes the last group) shows that the two streams really run at the same
+time.
 """
 
 import numpy as np
@@ -22,14 +24,15 @@ from gemm_tile_signaling_amd.pipeline import Pipeline  # noqa: E402
 
 
 @pytest.mark.parametrize("name,comp", [("profiled", (1, 1)), ("ar_prefill", (1, 1, 1, 1)), ("rs", (2, 2))])
-def test_consumer_overlaps_gemm(name, comp):
+@pytest.mark.parametrize("consumer", ["gated", "poll"])
+def test_consumer_overlaps_gemm(name, comp, consumer):
     w = WORKLOADS[name]
     A, B, peer, m_per, row_dest = make_inputs(w)
     o = make_plan(m_per, w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=comp, mode=w.mode, ranks=w.ranks)
     p = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp,
                 mode=w.mode, ranks=w.ranks)
-    say(f"overlap {name} {comp}")
-    pipe = Pipeline(p, to_dev(A), to_dev(B[0]), to_dev(peer))
+    say(f"overlap {name} {comp} consumer={consumer}")
+    pipe = Pipeline(p, to_dev(A), to_dev(B[0]), to_dev(peer), consumer=consumer)
     gtrace = torch.zeros(2 * p.NT + p.P, dtype=torch.int64, device="cuda")
     ctrace = torch.zeros(p.P, dtype=torch.int64, device="cuda")
     pipe.step()                                     # warm-up pass
