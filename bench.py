@@ -8,21 +8,26 @@ synthetic and already resident in HBM when the timed region starts.
 
 Default workload: the profiled GEMM shape of the pages' wave-pattern figure,
 M = 2048, N = K = 8192, bf16, 256 x 128 tiles, 512 tiles over 256 CUs (two
-waves), partitions (2) and (1, 1), the latter also with the post-reorder run
-group by group.  ``value`` is useful GEMM TFLOP/s of the whole step
-(2 M N K per step / step time) for the best of these schedules.
+waves).  Schedules: partitions (2) and (1, 1), the consumer gated in the
+stream's queue or polling on the CUs, the post-reorder whole or group by
+group.  The schedule is chosen from interleaved blocks; then, five times,
+W warm-up passes and exactly K timed passes (synchronised on both sides,
+host clock, with device events around the region); ``value`` is useful GEMM
+TFLOP/s of the whole step (2 M N K per step / step time) of the median
+region.
 
 Prints one JSON line.  Extra fields: the signaling and plain GEMMs measured
 alone (alternating blocks), their ratio, the consumer's and the
-post-reorder's HBM GB/s (MALL flushed before each timed launch), per-schedule
-pass times, the same pass without overlap, the other workloads, a check of
-the partition search, and the oracle timed on the host cores as a CPU
-baseline (rank 0, N = 1).
+post-reorder's HBM GB/s (MALL flushed before each timed launch; also on the
+224 MiB MoE layout), per-schedule pass times, the same pass without overlap,
+the other workloads, a check of the partition search, and the oracle timed
+on the host cores as a CPU baseline (rank 0, N = 1).
 """
 
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -86,12 +91,15 @@ def wave_pattern_of(t_sig, W, tick_us, bins=40):
             "bin_us": round(float(edges[1] - edges[0]), 3), "histogram": hist}
 
 
-def configs_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
+
+def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5):
     """The other workloads beside the headline: signaling and plain GEMM alone, and one pass of the
-    pipeline at each workload's first partition (one wave per group if it names none).
+    pipeline at each workload's first partition (one wave per group if it names none), gated consumer,
+    post-reorder group by group.
 
     Inputs are drawn on the device from the workload's distribution (the parity tests use the seeded host
-    inputs; throughput does not depend on the exact values).  MoE: useful FLOP count the routed rows only.
+    inputs; throughput does not depend on the exact values).  MoE: useful FLOP count the routed rows only;
+    its 224 MiB buffers also give the consumer's and the post-reorder's bandwidth beyond the MALL.
     """
     from workloads import WORKLOADS, moe_routing
     out = []
@@ -125,7 +133,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
         for _ in range(3):
             _sig(s)
         sig_ms, plain_ms = _time_pair(torch, _sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, 10)
-        pipe = Pipeline(plan, dA, dB, dpeer, streams=streams)
+        pipe = Pipeline(plan, dA, dB, dpeer, streams=streams, post_per_group=plan.P > 1)
         for _ in range(warmup):
             pipe.step()
         pipe.join()
@@ -139,14 +147,34 @@ def configs_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
             raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
         gemm_pipe_ms = float(np.median([e["gemm"][0].elapsed_time(e["gemm"][1]) for e in evs]))
         pass_ms = float(np.median([e["gemm"][0].elapsed_time(e["post"][1]) for e in evs]))
+        rec = {"workload": f"{name}: M={M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, {plan.NT} tiles, T={plan.T}, "
+                           f"mode {w.mode}, groups {list(comp) if comp else [1] * plan.T}, gated consumer, "
+                           f"post-reorder per group",
+               "signal_gemm_alone_tflops": round(flops / (sig_ms * 1e-3) / 1e12, 1),
+               "plain_gemm_alone_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 1),
+               "signal_over_plain_alone": round(plain_ms / sig_ms, 4),
+               "signal_gemm_in_pass_tflops": round(flops / (gemm_pipe_ms * 1e-3) / 1e12, 1),
+               "signal_in_pass_over_plain": round(plain_ms / gemm_pipe_ms, 4),
+               "frac_of_peak": round(flops / (gemm_pipe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "pass_ms": round(pass_ms, 4)}
+        if w.experts:
+            mn = M * w.N
+            status = torch.zeros(1, dtype=torch.int32, device=dev)
+            ready = plan.new_sig(dev)
+            plan.flag_of(ready).fill_(1)
+            recv = torch.empty_like(C)
+            cons_ms = _time_kernel(torch, lambda st: plan.consume_group(C, dpeer, recv, ready, 1, status, stream=st),
+                                   s, 10, scratch)
+            gated_ms = _time_kernel(torch, lambda st: plan.consume_group_gated(C, dpeer, recv, ready, 1, status,
+                                                                               stream=st), s, 10, scratch)
+            post_ms = _time_kernel(torch, lambda st: plan.reorder_post(recv, C, stream=st), s, 10, scratch)
+            rec.update(consumer_alone_gbps=round(6.0 * mn / (cons_ms * 1e-3) / 1e9, 1),
+                       consumer_gated_alone_gbps=round(6.0 * mn / (gated_ms * 1e-3) / 1e9, 1),
+                       post_reorder_alone_gbps=round(4.0 * mn / (post_ms * 1e-3) / 1e9, 1),
+                       hbm_note=f"{2 * mn / 2 ** 20:.0f} MiB per buffer, MALL flushed, event-timed")
+        out.append(rec)
         pipe.close()
-        out.append({"workload": f"{name}: M={M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, {plan.NT} tiles, T={plan.T}, "
-                                f"mode {w.mode}, groups {list(comp) if comp else [1] * plan.T}",
-                    "signal_gemm_alone_tflops": round(flops / (sig_ms * 1e-3) / 1e12, 1),
-                    "plain_gemm_alone_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 1),
-                    "signal_gemm_in_pass_tflops": round(flops / (gemm_pipe_ms * 1e-3) / 1e12, 1),
-                    "frac_of_peak": round(flops / (gemm_pipe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                    "pass_ms": round(pass_ms, 4)})
+        plan.close()
         del dA, dB, dpeer, C
     return out
 
@@ -160,8 +188,8 @@ def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
     stand-in, the consumer, run on a single group of each sampled size with
     the flag already raised (HIP events, so a call's fixed cost is included).
     fo_plan_search scores all 2^(T-1) partitions; every partition then runs in
-    the pipeline, and the measured end of communication (GEMM start to the
-    consumer's end) is set against the prediction.
+    the pipeline (gated consumer), and the measured end of communication (GEMM
+    start to the consumer's end) is set against the prediction.
     """
     from workloads import WORKLOADS, make_inputs
     w = WORKLOADS["ar_prefill"]
@@ -177,16 +205,19 @@ def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
     curve_b, curve_s = [], []
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     for rows in (16, 64, 256, 1024, 2048, 4096):
-        cp = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W)
-        cp = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=(cp.T,))
+        probe = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W)
+        cp = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=(probe.T,))
+        probe.close()
         x = torch.zeros(cp.M * cp.N, dtype=torch.int16, device=dev)
         y = torch.empty_like(x)
         ready = cp.new_sig(dev)
         cp.flag_of(ready).fill_(1)
-        ms = float(np.median([_time_kernel(torch, lambda st: cp.consume_group(x, x, y, ready, 1, status, stream=st),
+        ms = float(np.median([_time_kernel(torch, lambda st: cp.consume_group_gated(x, x, y, ready, 1, status,
+                                                                                    stream=st),
                                            s, 1) for _ in range(10)]))
         curve_b.append(2.0 * cp.M * cp.N)
         curve_s.append(ms * 1e-3)
+        cp.close()
     pred, pred_s, all_s = base.search(gemm_ms * 1e-3, curve_b, curve_s, with_all=True)
 
     def comp_of(mask, T):     # cut mask -> waves per group (bit i: a group ends after wave i+1)
@@ -214,12 +245,15 @@ def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
             raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
         meas = float(np.median([e["gemm"][0].elapsed_time(e["consume"][1]) for e in evs]))
         pipe.close()
+        plan.close()
         rows.append((comp, all_s[mask] * 1e3, meas))
+    T = base.T
+    base.close()
     best_m = min(rows, key=lambda r: r[2])
     pick = next(r for r in rows if r[0] == pred)
     order = sorted(rows, key=lambda r: r[2])
     return {
-        "workload": f"{w.name}: M={w.M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, wave {w.W}, T={base.T}",
+        "workload": f"{w.name}: M={w.M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, wave {w.W}, T={T}, gated consumer",
         "gemm_plain_us": round(gemm_ms * 1e3, 1),
         "curve_bytes": curve_b, "curve_us": [round(x * 1e6, 2) for x in curve_s],
         "predicted_best": list(pred), "predicted_us": round(pred_s * 1e6, 1),
@@ -281,33 +315,79 @@ def committed_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the GEMM kernel's sources and build flags: ties committed traffic counters to the code they measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("gemm_tile_signaling_amd/csrc/kernels/gemm.hip", "gemm_tile_signaling_amd/csrc/kernels/buffer.h",
+                "gemm_tile_signaling_amd/csrc/fo_internal.h", "gemm_tile_signaling_amd/build.py"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the signaling GEMM from the committed rocprofv3 counter passes, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"signal_gemm_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, min_seconds=10.0):
     """The oracle pipeline (fp64 GEMM, pre-reorder, consumer, post-reorder) on the host cores.
 
-    One pass over the whole workload takes about a second on a 16-core host,
-    so the bounded sample is the full workload, repeated until about
-    ``min_seconds`` of CPU work have been timed.
+    Threaded: the full workload, repeated until about ``min_seconds`` of CPU
+    work have been timed, with the BLAS thread pool at the host's CPU count.
+    Single-threaded: one pass over the first 512 rows of A (a quarter of the
+    profiled workload's rows, the same B), the BLAS pool at one thread.
     """
     import oracle
     from oracle.tiles import make_plan
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    plan = make_plan(m_per, w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=comp, mode=w.mode, ranks=w.ranks,
-                     row_dest=row_dest)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.run_pipeline(A, B, peer, plan, w.dtype)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= 50:
-            break
-    flops = 2.0 * w.M * w.N * w.K * reps
-    return dict(value=round(flops / dt / 1e12, 4), unit="TFLOP/s", cores=int(cores), kind="oracle",
+    from threadpoolctl import threadpool_info, threadpool_limits
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+    def run(rows, limit, min_s, max_reps):
+        Ar = A[:rows]
+        plan = make_plan([rows], w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W,
+                         composition=comp if rows == w.M else None, mode=w.mode, ranks=w.ranks, row_dest=row_dest)
+        pr = peer[:rows * w.N]
+        with threadpool_limits(limits=limit):
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.run_pipeline(Ar, B, pr, plan, w.dtype)
+                reps += 1
+                dt = time.perf_counter() - t0
+                if dt >= min_s or reps >= max_reps:
+                    break
+        return 2.0 * rows * w.N * w.K * reps / dt / 1e12, threads, reps, dt
+
+    v, threads, reps, dt = run(w.M, nproc, min_seconds, 50)
+    v1, _, reps1, dt1 = run(min(512, w.M), 1, 0.0, 1)
+    return dict(value=round(v, 4), unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample=f"full workload (M={w.M}, N={w.N}, K={w.K}, groups {tuple(comp)}) x {reps} passes, "
-                       f"{dt:.1f} s")
+                       f"{dt:.1f} s, BLAS pool {threads} threads",
+                single_thread=dict(value=round(v1, 4), unit="TFLOP/s",
+                                   sample=f"first {min(512, w.M)} rows x 1 pass, {dt1:.1f} s, 1 thread"),
+                nproc=int(nproc), cpu_model=_cpu_model())
 
 
 def main():
@@ -319,7 +399,7 @@ def main():
     import torch
     import gemm_tile_signaling_amd as fo
     from gemm_tile_signaling_amd.pipeline import Pipeline
-    from workloads import WORKLOADS, make_inputs, to_bits, draw
+    from workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[a.workload]
     if w.experts:
@@ -356,29 +436,50 @@ def main():
         for _ in range(a.steps):
             plan.consume_group(buf, dpeer, out, ready, 1, status)
         for _ in range(a.steps):
+            plan.consume_group_gated(buf, dpeer, out, ready, 1, status)
+        for _ in range(a.steps):
             plan.reorder_post(buf, out)
         torch.cuda.synchronize()
         print(json.dumps({"counters_pass": w.name, "launches_per_kernel": a.steps,
                           "calibration_copy_bytes": 256 * 2 ** 20, "status": int(status.item())}), flush=True)
+        plan.close()
         return
 
     # one pair of streams, each with a hardware queue of its own, for every pipeline and every kernel
     # timed alone: the device has few hardware queues, and streams created per pipeline would share
     # them in an order that changes the timings from one schedule to the next
     streams = (fo.stream_create(), fo.stream_create())
-    pipes = []   # one per schedule: a partition, with the post-reorder whole or group by group
+    plans, scheds = [], []   # schedules: a partition, the consumer, the post-reorder whole or per group
     for comp in comps:
         plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W,
                        composition=comp, mode=w.mode, ranks=w.ranks, row_dest=row_dest)
-        for per_group in ((False, True) if plan.P > 1 else (False,)):
-            pipes.append(dict(plan=plan, pipe=Pipeline(plan, dA, dB, dpeer, post_per_group=per_group,
-                                                       streams=streams),
-                              comp=comp or tuple([1] * plan.T), per_group=per_group))
+        plans.append(plan)
+        for consumer in ("gated", "poll"):
+            for per_group in ((False, True) if plan.P > 1 else (False,)):
+                scheds.append(dict(plan=plan, pipe=Pipeline(plan, dA, dB, dpeer, post_per_group=per_group,
+                                                            streams=streams, consumer=consumer),
+                                   comp=comp or tuple([1] * plan.T), per_group=per_group, consumer=consumer))
     launches = [0]   # signaling-GEMM launches so far (locates the timed region in a kernel trace)
-    # every event is created here: creating a few hundred takes tens of milliseconds, and the GPU
-    # idling that long between the warm-up and the timed passes starts them in a clock transient
-    gemm_ev = _event_pairs(torch, a.steps)
-    br_ev = [{k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")} for _ in pipes]
+    regions = 5
+    # every event is created and recorded once here: torch creates the HIP event at its first
+    # record, and a few hundred creations inside a timed loop stall the host for milliseconds;
+    # the GPU idling that long drops its clock, and the passes after it run in the ramp back up
+    gemm_ev = [_event_pairs(torch, a.steps) for _ in range(regions)]
+    region_ev = _event_pairs(torch, regions)
+    pick_ev = _event_pairs(torch, a.steps)
+    br_ev = [{k: _event_pairs(torch, a.steps) for k in ("gemm", "consume", "post")} for _ in scheds]
+    for pair in ([p for r in gemm_ev for p in r] + region_ev + pick_ev
+                 + [p for d in br_ev for v in d.values() for p in v]):
+        pair[0].record()
+        pair[1].record()
+    torch.cuda.synchronize()
+    # no garbage collection pause inside the measured phases either
+    gc.collect()
+    gc.disable()
+
+    def check(pipe):
+        if int(pipe.status.item()) != 0:
+            raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
 
     def passes(pipe, n, **kw):
         for _ in range(n):
@@ -386,62 +487,80 @@ def main():
         launches[0] += n
         pipe.join()
         torch.cuda.synchronize()
-        if int(pipe.status.item()) != 0:
-            raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
+        check(pipe)
 
-    # choose the partition: blocks of K passes, every schedule in turn, three rounds, so that
-    # clock and power drift falls on all of them alike; the serial schedule (GEMM, then consumer,
-    # then post-reorder, one queue) is measured the same way for comparison
-    passes(pipes[0]["pipe"], a.warmup)
-    n_pick = a.steps
-    sched = [(i, False) for i in range(len(pipes))] + [(0, True)]
-    picks = {k: [] for k in sched}
+    # choose the schedule: blocks of K passes (each GEMM bracketed by events, as in the timed
+    # region), every schedule in turn, three rounds, so that clock and power drift falls on all of
+    # them alike; the serial schedule (GEMM, consumer, post-reorder on one queue) is measured alike
+    passes(scheds[0]["pipe"], a.warmup)
+    order = [(i, False) for i in range(len(scheds))] + [(0, True)]
+    picks = {k: [] for k in order}
     for _ in range(3):
-        for i, serial in sched:
-            passes(pipes[i]["pipe"], 5, serial=serial)
+        for i, serial in order:
+            pipe = scheds[i]["pipe"]
+            passes(pipe, 5, serial=serial)
             t0 = time.perf_counter()
-            passes(pipes[i]["pipe"], n_pick, serial=serial)
-            picks[(i, serial)].append((time.perf_counter() - t0) * 1e3 / n_pick)
-    for i, r in enumerate(pipes):
+            for j in range(a.steps):
+                pipe.step(events={"gemm": pick_ev[j]}, serial=serial)
+            pipe.join()
+            torch.cuda.synchronize()
+            picks[(i, serial)].append((time.perf_counter() - t0) * 1e3 / a.steps)
+            launches[0] += a.steps
+            check(pipe)
+    for i, r in enumerate(scheds):
         r["pick_ms"] = float(np.median(picks[(i, False)]))
     serial_ms = float(np.median(picks[(0, True)]))
-    best = min(pipes, key=lambda r: r["pick_ms"])
+    best = min(scheds, key=lambda r: r["pick_ms"])
     plan, pipe = best["plan"], best["pipe"]
 
-    # timed: W warm-up passes, then K passes of the chosen partition; only the GEMM is bracketed by
-    # events (on its own stream), since every event is a packet in a hardware queue and adds to the pass
-    passes(pipe, a.warmup)
-    timed_first = launches[0]
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        pipe.step(events={"gemm": gemm_ev[i]})
-    launches[0] += a.steps
-    pipe.join()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    if int(pipe.status.item()) != 0:
-        raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
-    gemm_each = [s.elapsed_time(e) for s, e in gemm_ev]
-    best.update(step_ms=el * 1e3 / a.steps, gemm_ms=float(np.mean(gemm_each)),
-                gemm_q=np.percentile(gemm_each, [10, 50, 90]).tolist())
-    timed_range = [timed_first, launches[0]]
+    # timed: five regions, each W warm-up passes then exactly K passes of the chosen schedule,
+    # synchronised on both sides; a device event pair brackets each region (first GEMM's start to
+    # the last post-reorder's end) beside the host clock; the GEMM of every pass is bracketed by
+    # events on its own stream for the roofline.  The value is the median region.  Before the
+    # first region the chosen schedule runs 100 untimed passes, so no region starts in a clock ramp.
+    passes(pipe, 100)
+    reg = []
+    for r in range(regions):
+        passes(pipe, a.warmup)
+        first = launches[0]
+        t0 = time.perf_counter()
+        region_ev[r][0].record(pipe.next_gemm_stream())
+        for i in range(a.steps):
+            pipe.step(events={"gemm": gemm_ev[r][i]})
+        region_ev[r][1].record(pipe.post_stream)
+        pipe.join()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+        launches[0] += a.steps
+        check(pipe)
+        each = [s.elapsed_time(e) for s, e in gemm_ev[r]]
+        dev_ms = region_ev[r][0].elapsed_time(region_ev[r][1]) / a.steps
+        reg.append(dict(host_ms=host_ms, device_ms=dev_ms, gemm_ms=float(np.mean(each)),
+                        gemm_q=np.percentile(each, [10, 50, 90]).tolist(), launches=[first, launches[0]]))
+    mid = sorted(range(regions), key=lambda r: reg[r]["host_ms"])[regions // 2]
+    best.update(step_ms=reg[mid]["host_ms"], gemm_ms=reg[mid]["gemm_ms"], gemm_q=reg[mid]["gemm_q"])
+    timed_range = reg[mid]["launches"]
 
-    # untimed: every kernel of every partition bracketed, for the breakdown
-    for r, evs in zip(pipes, br_ev):
+    # untimed: every kernel of every schedule bracketed, for the breakdown
+    for r, evs in zip(scheds, br_ev):
         for i in range(a.steps):
             r["pipe"].step(events={k: v[i] for k, v in evs.items()})
         launches[0] += a.steps
         r["pipe"].join()
         torch.cuda.synchronize()
+        check(r["pipe"])
         avg = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in evs.items()}
         r.update(br_gemm_ms=avg["gemm"], consume_ms=avg["consume"], post_ms=avg["post"])
 
-    # one traced pass: device wall-clock stamps of every tile's signal and of each consumer wait
+    gc.enable()
+
+    # one traced pass: device wall-clock stamps of every tile's signal and of each group's consumer start
     gtr = torch.zeros(2 * plan.NT + plan.P, dtype=torch.int64, device=dev)
     ctr = torch.zeros(plan.P, dtype=torch.int64, device=dev)
     pipe.step(trace=gtr, consumer_trace=ctr)
     pipe.join()
     torch.cuda.synchronize()
+    check(pipe)
     g = gtr.cpu().numpy().view(np.uint64).astype(np.int64)
     c = ctr.cpu().numpy().view(np.uint64).astype(np.int64)
     tick_us = 1e3 / plan.info["clock_khz"]
@@ -470,6 +589,8 @@ def main():
     recv = torch.empty_like(pipe.buf)
     consume_ms = _time_kernel(torch, lambda st: plan.consume_group(pipe.buf, dpeer, recv, ready, 1, status, stream=st),
                               s, n_alone, scratch)
+    gated_ms = _time_kernel(torch, lambda st: plan.consume_group_gated(pipe.buf, dpeer, recv, ready, 1, status,
+                                                                       stream=st), s, n_alone, scratch)
     post_ms = _time_kernel(torch, lambda st: plan.reorder_post(recv, C, stream=st), s, n_alone, scratch)
     bias = (torch.randn(plan.num_problems * w.N, device=dev) * 0.02).to(torch.bfloat16 if w.dtype == "bf16"
                                                                         else torch.float16).view(torch.int16)
@@ -490,6 +611,7 @@ def main():
     del c_mat
     mn = w.M * w.N
     consume_gbps = 6.0 * mn / (consume_ms * 1e-3) / 1e9
+    gated_gbps = 6.0 * mn / (gated_ms * 1e-3) / 1e9
     post_gbps = 4.0 * mn / (post_ms * 1e-3) / 1e9
 
     achieved = flops / (best["gemm_ms"] * 1e-3) / 1e12
@@ -503,15 +625,20 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: GEMM M={w.M} N={w.N} K={w.K} {w.dtype}, {w.BM}x{w.BN} tiles, "
                                f"swizzle {w.S}, wave {w.W} tiles, groups {tuple(best['comp'])}, "
-                               f"consumer copy+add, post-reorder{' per group' if best['per_group'] else ''}",
+                               f"{best['consumer']} consumer copy+add, "
+                               f"post-reorder{' per group' if best['per_group'] else ''}",
                    "M": w.M, "N": w.N, "K": w.K, "tile": [w.BM, w.BN], "swizzle": w.S, "wave": w.W,
-                   "tiles": plan.NT, "waves": plan.T, "groups": list(best["comp"]),
+                   "tiles": plan.NT, "waves": plan.T, "groups": list(best["comp"]), "consumer": best["consumer"],
                    "post_per_group": best["per_group"], "parallelism": "1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(w.name),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes": 2 * (w.M * w.K + w.N * w.K + w.M * w.N),
-                     "kernel": "signaling GEMM (stream A, consumer resident)"},
+                     "kernel": "signaling GEMM inside the timed passes (events on its own stream)"},
+        "timed_regions": [{"host_ms_per_step": round(r["host_ms"], 4), "device_ms_per_step": round(r["device_ms"], 4),
+                           "signal_gemm_ms": round(r["gemm_ms"], 4)} for r in reg],
+        "timed_region_used": mid,
+        "choice_block_ms_per_step": round(best["pick_ms"], 4),
         "signal_gemm_us_p10_p50_p90": [round(x * 1e3, 1) for x in best["gemm_q"]],
         "serial_pass_ms": round(serial_ms, 4),
         "overlap_speedup_over_serial": round(serial_ms / best["pick_ms"], 4),
@@ -521,25 +648,36 @@ def main():
         "signal_with_consumer_over_plain": round(plain_ms / best["gemm_ms"], 4),
         "context_library_gemm_tflops": round(flops / (lib_ms * 1e-3) / 1e12, 2),
         "consumer_alone_gbps": round(consume_gbps, 1),
+        "consumer_gated_alone_gbps": round(gated_gbps, 1),
         "post_reorder_alone_gbps": round(post_gbps, 1),
-        "post_reorder_bias_silu_alone_gbps": round((4.0 * mn + 2.0 * plan.num_problems * w.N) / (post_ep_ms * 1e-3) / 1e9,
-                                                   1),
-        "consumer_frac_hbm": round(consume_gbps / PEAK_HBM_GBPS, 4),
+        "post_reorder_bias_silu_alone_gbps": round((4.0 * mn + 2.0 * plan.num_problems * w.N) / (post_ep_ms * 1e-3)
+                                                   / 1e9, 1),
+        "consumer_frac_hbm": round(max(consume_gbps, gated_gbps) / PEAK_HBM_GBPS, 4),
         "post_reorder_frac_hbm": round(post_gbps / PEAK_HBM_GBPS, 4),
         "signal_to_consume_us": signal_to_consume_us,
         "first_group_consumed_before_gemm_end_us": first_consume_before_gemm_end_us,
         "wave_pattern": wave_pattern,
-        "partitions": [{"groups": list(r["comp"]), "post_per_group": r["per_group"],
-                        "pick_step_ms": round(r["pick_ms"], 4),
-                        "gemm_ms": round(r["br_gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
-                        "post_ms": round(r["post_ms"], 4)} for r in pipes],
+        "schedules": [{"groups": list(r["comp"]), "consumer": r["consumer"], "post_per_group": r["per_group"],
+                       "pick_step_ms": round(r["pick_ms"], 4),
+                       "gemm_ms": round(r["br_gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
+                       "post_ms": round(r["post_ms"], 4)} for r in scheds],
         "timed_signal_gemm_launches": timed_range,
         "cpu_baseline": None,
     }
+    for r in scheds:
+        r["pipe"].close()
     if not a.no_configs:
-        line["configs"] = configs_check(torch, fo, Pipeline, dev, streams)
+        line["configs"] = configs_check(torch, fo, Pipeline, dev, streams, scratch)
     if not a.no_search:
         line["search"] = search_check(torch, fo, Pipeline, dev, streams)
+    # release every device object before the interpreter exits
+    torch.cuda.synchronize()
+    for st in streams:
+        fo.stream_destroy(st)
+    for p_ in plans:
+        p_.close()
+    del scheds, pipe, plan
+    torch.cuda.synchronize()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, peer, m_per, row_dest, best["comp"])
     print(json.dumps(line), flush=True)

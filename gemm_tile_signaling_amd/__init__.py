@@ -317,7 +317,7 @@ class Plan:
 
     def consume_group_gated(self, send, peer, recv, sig, epoch: int, status, g_begin: int = 0,
                             g_end: Optional[int] = None, trace=None, stream=None):
-        """Consumer waiting in the stream's queue for each group's flag (``fo_consume_group_gated``)."""
+        """Consumer gated by a stream wait on each group's flag (``fo_consume_group_gated``)."""
         g_end = self.P if g_end is None else g_end
         _check(lib().fo_consume_group_gated(
             self._h, _ptr(send, numel=self.mn, itemsize=2, name="send"),

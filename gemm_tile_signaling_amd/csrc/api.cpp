@@ -95,7 +95,7 @@ int fo_consume_group_gated(const fo_plan *p, const void *send, const void *peer,
   if (!p->can_wait_value) return FO_ERR_UNSUPPORTED;
   const uint32_t *flag = sig + p->flag_offset();
   for (int32_t g = g_begin; g < g_end; ++g) {
-    // the stream's queue waits until flag[g] >= epoch, then runs the group's kernel
+    // the stream proceeds once flag[g] >= epoch (a stream wait), then runs the group's kernel
     if (hipStreamWaitValue32(stream, const_cast<uint32_t *>(flag + g), epoch, hipStreamWaitValueGte, 0xFFFFFFFFu) !=
         hipSuccess)
       return FO_ERR_HIP;

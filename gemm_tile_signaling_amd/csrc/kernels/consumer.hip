@@ -28,10 +28,10 @@
 // stores past the end are dropped.  The kernel holds no LDS beyond one word
 // and few registers, so it can stay resident next to the GEMM's workgroups.
 //
-// The same kernel also runs as the second half of the gated consumer: the
-// stream's hardware queue waits for the group's flag (hipStreamWaitValue32)
-// and only then launches it over that one group, with a grid sized to the
-// span; its single check of the flag then passes at once.
+// The same kernel also runs as the second half of the gated consumer: a
+// stream wait for the group's flag (hipStreamWaitValue32) is enqueued ahead
+// of it, and it runs over that one group with a grid sized to the span; its
+// single check of the flag then passes at once.
 //
 // Epoch stamps (optional, a plan flag): after a group's wait every workgroup
 // reads its share of the group's per-slot stamps with the same device-coherent
@@ -198,7 +198,7 @@ int launch_consume(const fo_plan *p, const void *send, const void *peer, void *r
 
 int launch_consume_ready(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
                          uint32_t epoch, int32_t g, int32_t *status, uint64_t *trace, hipStream_t s) {
-  // launched behind the queue's wait for the flag: the kernel's own wait passes at once
+  // enqueued behind a stream wait for the flag: the kernel's own wait passes at once
   const ConsumeParams cp = params(p, send, peer, recv, sig, epoch, g, g + 1, status, 2000000ull * p->ticks_per_us,
                                   trace);
   const int64_t chunks = (p->unit_off[p->group_unit[g + 1]] - p->unit_off[p->group_unit[g]]) / 8;

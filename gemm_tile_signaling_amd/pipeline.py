@@ -15,10 +15,10 @@ as the previous GEMM on its queue ends, but it touches its buffers only once
 a flag of its own epoch is raised, i.e. after this pass's GEMM has started,
 which is after the previous post-reorder (the last reader of recv) ended.
 
-Consumer: ``consumer="gated"`` (the default) enqueues, per group, a wait in
-the stream's hardware queue for the group's flag and then a streaming kernel
-over the span (``fo_consume_group_gated``): nothing occupies a CU until the
-group is signalled.  ``consumer="poll"`` runs the persistent consumer that
+Consumer: ``consumer="gated"`` (the default) enqueues, per group, a stream
+wait for the group's flag (one polling wave, in the runtime's implementation)
+and then a streaming kernel over the span (``fo_consume_group_gated``): the
+span kernel starts only once the group is signalled.  ``consumer="poll"`` runs the persistent consumer that
 polls the flags on the CUs (``fo_consume_group``), one workgroup per CU beside
 the GEMM.
 
@@ -150,6 +150,10 @@ class Pipeline:
                 ev["post"][1].record(s_comm)
         self.post_stream = s_comm
         return e
+
+    def next_gemm_stream(self):
+        """The stream the next overlapped pass will launch its GEMM on (the streams swap roles every pass)."""
+        return self.sa if (self.epoch + 1) % 2 == 0 else self.sb
 
     def _consume(self, epoch, g0, g1, consumer_trace, stream):
         p = self.plan

@@ -324,16 +324,18 @@ int fo_consume_group(const fo_plan *plan, const void *send, const void *peer, vo
                      uint64_t *trace, hipStream_t stream);
 
 /*
- * Consumer waiting in the command processor instead of on the CUs
+ * Consumer gated by a stream wait instead of a persistent polling grid
  * (deep-dive 五 › 专用监控内核: the signal may reach the transfer stream as an
  * event-like notification rather than through a polling kernel).  For g =
  * g_begin .. g_end-1 in order it enqueues on `stream` a wait until flag[g] >=
- * epoch (hipStreamWaitValue32, evaluated by the stream's hardware queue) and
- * then a streaming kernel over g's span with the same arithmetic as
- * fo_consume_group:  recv[u] = round(float(send[u]) + float(peer[u])).  The
- * kernel is launched only once the group is signalled, so it never occupies a
- * CU while it waits, and its grid is sized to the span (several workgroups
- * per CU) instead of being persistent.
+ * epoch (hipStreamWaitValue32; the HIP runtime of ROCm 7 carries it out as a
+ * one-thread kernel that polls the word, so a single wave waits instead of a
+ * workgroup on every CU) and then a streaming kernel over g's span with the
+ * same arithmetic as fo_consume_group:
+ *   recv[u] = round(float(send[u]) + float(peer[u])).
+ * The streaming kernel starts only once the group is signalled, and its grid
+ * is sized to the span (several workgroups per CU) instead of being
+ * persistent, so nothing of it waits on a CU for the GEMM.
  * The wait has no time limit: the signaling GEMM of `epoch` on the same sig
  * must be enqueued (on another stream) or the stream never proceeds.
  * dev_status: device int32 as for fo_consume_group; receives FO_ERR_STALE

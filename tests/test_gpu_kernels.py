@@ -395,7 +395,7 @@ def test_every_kernel_with_buffers_above_bit31_of_the_low_word():
 
 @pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])
 def test_consumer_gated_bit_exact(entry):
-    """The consumer whose stream's queue waits for each flag: bit-exact against the oracle over all groups,
+    """The consumer gated by a stream wait on each flag: bit-exact against the oracle over all groups,
     and over a range of groups (the rest of recv untouched)."""
     o, p = _plans(entry)
     dt = entry[4]

@@ -2,7 +2,7 @@
 
 Both kernels stamp the device wall clock: the GEMM when each tile signals,
 the consumer when its wait for a group ends (the polling consumer) or when
-the group's kernel starts behind the queue's wait (the gated consumer).
+the group's kernel starts behind its stream wait (the gated consumer).
 Causality (a group is consumed only after its last tile signalled) must hold
 for every group; overlap (the first group is consumed while the GEMM still
 computes the last group) shows that the two streams really run at the same

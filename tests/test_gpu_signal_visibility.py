@@ -9,8 +9,9 @@ same magnitudes, the opposite sign, so every element of C changes), the
 reorder buffer, recv and every pass's own output start as a NaN marker, and
 every pass's output is checked element by element against the oracle.  The
 plans carry epoch stamps (FO_PLAN_EPOCH_STAMPS), which the consumer checks
-after each signal.  Both consumers run: the gated one (the stream's queue
-waits for the flag) and the polling one (a persistent kernel on the CUs).
+after each signal.  Both consumers run: the gated one (a stream wait on the
+flag, then a kernel over the span) and the polling one (a persistent kernel
+on the CUs).
 
 The stale-read detector itself is exercised by forcing its condition from
 the host: flags raised by hand, stamps left at an old epoch; the consumer must
