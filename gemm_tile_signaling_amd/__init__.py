@@ -87,6 +87,7 @@ def lib() -> C.CDLL:
             "fo_gemm_signal": [vp, vp, vp, vp, vp, u32, vp, vp],
             "fo_gemm_plain": [vp, vp, vp, vp, vp],
             "fo_gemm_signal_serialized": [vp, vp, vp, vp, vp, u32, vp, vp],
+            "fo_gemm_signal_noalloc": [vp, vp, vp, vp, vp, vp, vp],
             "fo_consume_group": [vp, vp, vp, vp, vp, u32, i32, i32, vp, u64, i32, vp, vp],
             "fo_consume_group_gated": [vp, vp, vp, vp, vp, u32, i32, i32, vp, vp, vp],
             "fo_reorder_shards": [vp, vp, vp, vp],
@@ -287,6 +288,18 @@ class Plan:
             _ptr(reorder_buf, numel=self.mn, itemsize=2, name="reorder_buf"),
             _ptr(sig, numel=self.sig_words, itemsize=4, name="sig"), int(epoch),
             _ptr(trace, numel=2 * self.NT + self.P, itemsize=8, name="trace"), _stream(stream)), "fo_gemm_signal")
+
+    def gemm_signal_noalloc(self, A, B, reorder_buf, stream=None):
+        """``fo_gemm_signal_noalloc``: the signal words live in the library's own device array.
+        Returns (device address of the signal words, epoch) for the consumer of this launch."""
+        sig = C.c_void_p()
+        epoch = C.c_uint32()
+        _check(lib().fo_gemm_signal_noalloc(
+            self._h, _ptr(A, numel=self.M * self.K, itemsize=2, name="A"),
+            _ptr(B, numel=self.num_problems * self.N * self.K, itemsize=2, name="B"),
+            _ptr(reorder_buf, numel=self.mn, itemsize=2, name="reorder_buf"), C.byref(sig), C.byref(epoch),
+            _stream(stream)), "fo_gemm_signal_noalloc")
+        return int(sig.value or 0), int(epoch.value)
 
     def gemm_signal_serialized(self, A, B, reorder_buf, sig, epoch: int, snapshots, stream=None):
         """Debug form with a device-wide barrier after every wave (``fo_gemm_signal_serialized``);

@@ -123,8 +123,11 @@ struct fo_plan {
 namespace fo {
 
 // Kernel launchers (the .hip files).  Arguments are validated by the caller.
+// counts_cleared: the counting table was zeroed for this launch, so a group fires at |G_g|
+// instead of epoch * |G_g| (the signal words are otherwise monotonic across epochs)
 int launch_gemm(const fo_plan *p, const void *A, const void *B, void *C, bool rowmajor,
-                uint32_t *sig, uint32_t epoch, uint64_t *trace, uint32_t *serial, hipStream_t s);
+                uint32_t *sig, uint32_t epoch, uint64_t *trace, uint32_t *serial, hipStream_t s,
+                bool counts_cleared = false);
 int launch_consume(const fo_plan *p, const void *send, const void *peer, void *recv,
                    const uint32_t *sig, uint32_t epoch, int32_t g_begin, int32_t g_end,
                    int32_t *status, uint64_t timeout_ticks, int32_t grid, uint64_t *trace, hipStream_t s);

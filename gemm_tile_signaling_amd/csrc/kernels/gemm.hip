@@ -168,6 +168,8 @@ struct GemmParams {
   uint64_t *trace;
   uint32_t *stamps;        // NULL, or one word per slot: the epoch, once the slot's tile is stored
   uint32_t epoch;
+  uint32_t fire_mult;      // group g fires when its counter reaches fire_mult * |G_g| (epoch, or 1 when
+                           // the counters were cleared for this launch)
   int32_t P;
   uint32_t *serial;        // serialized waves only: snapshots [T][2P], then barrier counter, then status
   uint64_t timeout_ticks;  // serialized waves only: bound on one barrier wait
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         if (p.stamps) __hip_atomic_store(&p.stamps[b], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(&p.cnt[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool fire = old + 1u == p.epoch * (uint32_t)p.thr[grp];
+        const bool fire = old + 1u == p.fire_mult * (uint32_t)p.thr[grp];
         if (fire) __hip_atomic_store(&p.flag[grp], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         if (p.trace) {
           p.trace[2 * (int64_t)b] = wall_clock64();
@@ -553,7 +555,7 @@ int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
 }  // namespace
 
 int launch_gemm(const fo_plan *p, const void *A, const void *B, void *Cout, bool rowmajor, uint32_t *sig,
-                uint32_t epoch, uint64_t *trace, uint32_t *serial, hipStream_t s) {
+                uint32_t epoch, uint64_t *trace, uint32_t *serial, hipStream_t s, bool counts_cleared) {
   if (p->NT == 0) return FO_OK;
   GemmParams gp{};
   gp.A = static_cast<const uint16_t *>(A);
@@ -574,6 +576,7 @@ int launch_gemm(const fo_plan *p, const void *A, const void *B, void *Cout, bool
   gp.trace = sig ? trace : nullptr;
   gp.stamps = sig && p->stamps() ? sig + p->stamp_offset() : nullptr;
   gp.epoch = epoch;
+  gp.fire_mult = counts_cleared ? 1u : epoch;
   gp.P = p->P;
   gp.serial = serial;
   gp.timeout_ticks = 2000000ull * p->ticks_per_us;  // 2 s per barrier wait

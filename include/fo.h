@@ -263,6 +263,30 @@ int fo_gemm_signal(const fo_plan *plan, const void *A, const void *B, void *reor
                    uint32_t *sig, uint32_t epoch, uint64_t *trace, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * launch as fo_gemm_signal, with the signal words (counting table, flags and,
+ * for FO_PLAN_EPOCH_STAMPS plans, the stamps) kept in a fixed array of the
+ * library's own device memory instead of a caller buffer: 16384 words
+ * (64 KiB) per device, held until the process ends.  Plans whose sig_words
+ * exceed 16384 are refused with FO_ERR_UNSUPPORTED before anything is
+ * enqueued.  No allocation: the array's address is looked up once per device
+ * (hipGetSymbolAddress, at the first call on that device).
+ *
+ * The library chooses the epoch (a counter per device, 1, 2, ...), clears the
+ * plan's sig_words words of the array with a small kernel on `stream` ahead
+ * of the GEMM (an earlier plan may have left counters where this one keeps
+ * its flags), and the GEMM fires each group at |G_j| tiles.  *sig_out receives the array's device
+ * address and *epoch_out the epoch: pass both to fo_consume_group or
+ * fo_consume_group_gated for this launch's groups.  Every call on a device
+ * shares that device's array, which keeps the last call's contents: calls
+ * whose GEMMs or consumers overlap on one device race on it, so issue them in
+ * order.  A, B and reorder_buf as for fo_gemm_signal.
+ */
+int fo_gemm_signal_noalloc(const fo_plan *plan, const void *A, const void *B, void *reorder_buf,
+                           uint32_t **sig_out, uint32_t *epoch_out, hipStream_t stream);
+
+/*
  * Debug form of fo_gemm_signal that makes the waves physical, so that the
  * counting table's trajectory (deep-dive 一 › 实现方法, the worked example's
  * table after every wave) can be read back: after wave w every workgroup
