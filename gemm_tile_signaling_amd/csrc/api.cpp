@@ -4,8 +4,6 @@
 #include <cstdint>
 #include <vector>
 
-#include <hip/hip_ext.h>
-
 #include "fo_internal.h"
 
 namespace {
