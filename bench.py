@@ -105,8 +105,12 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
     out = []
     s = streams[0]
     td = {"bf16": torch.bfloat16, "fp16": torch.float16}
-    for name in ("ar_prefill", "ar_decode", "rs", "moe_a2a"):
+    # the prefill, ReduceScatter and MoE shapes keep two or more waves with 256 x 256 tiles as well
+    runs = [("ar_prefill", None), ("ar_prefill", (256, 256)), ("ar_decode", None), ("rs", None), ("rs", (256, 256)),
+            ("moe_a2a", None), ("moe_a2a", (256, 256))]
+    for name, tile in runs:
         w = WORKLOADS[name]
+        BM, BN = tile or (w.BM, w.BN)
         if w.experts:
             m_per, tok = moe_routing(w)
             row_dest = tok // (w.tokens // w.ranks)
@@ -119,8 +123,8 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
         dA = (torch.randn(M * w.K, device=dev, generator=g) * std).to(td[w.dtype]).view(torch.int16)
         dB = (torch.randn(len(m_per) * w.N * w.K, device=dev, generator=g) * std).to(td[w.dtype]).view(torch.int16)
         dpeer = (torch.randn(M * w.N, device=dev, generator=g) * std).to(td[w.dtype]).view(torch.int16)
-        comp = w.compositions[0] if w.compositions else None
-        plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp,
+        comp = w.compositions[0] if w.compositions and tile is None else None
+        plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=BM, BN=BN, swizzle=w.S, wave_size=w.W, composition=comp,
                        mode=w.mode, ranks=w.ranks, row_dest=row_dest)
         flops = 2.0 * M * w.N * w.K
         C = torch.empty(M * w.N, dtype=torch.int16, device=dev)
@@ -147,7 +151,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
             raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
         gemm_pipe_ms = float(np.median([e["gemm"][0].elapsed_time(e["gemm"][1]) for e in evs]))
         pass_ms = float(np.median([e["gemm"][0].elapsed_time(e["post"][1]) for e in evs]))
-        rec = {"workload": f"{name}: M={M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, {plan.NT} tiles, T={plan.T}, "
+        rec = {"workload": f"{name}: M={M} N={w.N} K={w.K}, {BM}x{BN} tiles, {plan.NT} tiles, T={plan.T}, "
                            f"mode {w.mode}, groups {list(comp) if comp else [1] * plan.T}, gated consumer, "
                            f"post-reorder per group",
                "signal_gemm_alone_tflops": round(flops / (sig_ms * 1e-3) / 1e12, 1),
@@ -157,7 +161,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
                "signal_in_pass_over_plain": round(plain_ms / gemm_pipe_ms, 4),
                "frac_of_peak": round(flops / (gemm_pipe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                "pass_ms": round(pass_ms, 4)}
-        if w.experts:
+        if w.experts and tile is None:
             mn = M * w.N
             status = torch.zeros(1, dtype=torch.int32, device=dev)
             ready = plan.new_sig(dev)

@@ -20,21 +20,23 @@
 //     A and B fragments are passed to the MFMA swapped (B as the first
 //     operand) so that every lane ends up with 4 consecutive columns of one
 //     output row, which the epilogue writes as 8-byte pieces.
-//   * BK = 64; A and B K-slices go from memory straight into LDS (gfx950
+//   * K-slices of BK = 64 (32 for the 256 x 256 tile, whose stages are twice
+//     as large): A and B K-slices go from memory straight into LDS (gfx950
 //     buffer loads with the LDS destination, 16 bytes per lane), through a
 //     ring of LDS stages (three; six for 64 x 64 tiles, which have little
-//     arithmetic per slice to hide a load behind): slice k+2 (k+5) is loaded while slice k is
-//     multiplied, its DMA instructions spread over the multiplication so the
-//     wave never waits on a full memory queue with the matrix pipe idle; no
-//     VGPRs or ds_write instructions are spent on staging.
-//   * LDS rows are 128 bytes (64 K-elements); 16-byte chunk c of row r is
-//     stored at chunk c ^ ((r / 2) % 8).  gfx950's LDS serves 16 lanes of a
+//     arithmetic per slice to hide a load behind; four half-depth stages for
+//     256 x 256): slice k+NS-1 is loaded while slice k is multiplied, its DMA
+//     instructions spread over the slice's k-steps so the wave never waits on
+//     a full memory queue with the matrix pipe idle; no VGPRs or ds_write
+//     instructions are spent on staging.
+//   * LDS rows are BK * 2 bytes; 16-byte chunk c of row r is stored at chunk
+//     c ^ ((r / WR) % CHUNKS), WR rows sharing one 256-byte window of the 64
+//     banks (BK = 64: c ^ ((r / 2) % 8)).  gfx950's LDS serves 16 lanes of a
 //     ds_read_b128 per cycle over 64 banks (256 bytes): the 16 lanes read the
 //     same K-chunk of 16 consecutive rows, which this swizzle spreads over all
-//     64 banks (rows r and r+1 start in different halves of the banks, and
-//     the XOR term separates the 8 row pairs).  A DMA load writes lane l's 16
-//     bytes at position l of the wave's 1 KiB destination, so each lane
-//     fetches the global chunk that belongs at its position.
+//     64 banks.  A DMA load writes lane l's 16 bytes at position l of the
+//     wave's 1 KiB destination, so each lane fetches the global chunk that
+//     belongs at its position.
 //   * The MFMA accumulators live in the accumulation registers (AGPRs); the
 //     LDS reads of k-step s+1 are issued between the MFMAs of k-step s.
 //   * Each wave waits for its own loads of slice k, then the workgroup meets
@@ -60,6 +62,8 @@
 //   * A third instantiation serializes the waves for tests and traces (a
 //     device-wide barrier and a snapshot of the signal words after every
 //     wave, cooperative launch); the hot path never runs it.
+#include <type_traits>
+
 #include "../fo_internal.h"
 #include "buffer.h"
 
@@ -76,8 +80,6 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;
-constexpr int kRowBytes = BK * 2;               // one staged row of A or B
 constexpr int kVmcntZero = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 constexpr int kLgkmcntZero = 0xC07F;            // s_waitcnt lgkmcnt(0), other counters unconstrained
 // Cache policy of the output stores: system scope (sc0 | sc1), i.e. written
@@ -222,27 +224,46 @@ __device__ __forceinline__ bool wave_snapshot(const GemmParams &p, int w) {
   return grid_barrier(bar, status, 2u * w + 1u, p.timeout_ticks);
 }
 
-template <int BM, int BN>
+// Tile BM x BN, K-slices of BK (64 or 32) staged in LDS.
+template <int BM, int BN, int BK>
 struct Cfg {
+  static constexpr int ROWB = BK * 2;                 // bytes of one staged row of A or B
+  static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per staged row
+  static constexpr int KS = BK / 16;                  // MFMA k-steps per slice
+  static constexpr int RPK = 1024 / ROWB;             // staged rows per KiB (one DMA instruction of a wave)
+  static constexpr int WR = 256 / ROWB;               // rows that share one 256-byte window of the 64 banks
   // LDS ring depth: slice k+NS-1 is loaded while slice k is multiplied.  Small
-  // tiles have little arithmetic per slice, so they keep more slices in flight.
-  static constexpr int NS = BM == 64 ? 6 : 3;
+  // tiles have little arithmetic per slice, so they keep more slices in flight;
+  // half-depth slices (BK = 32) let a ring of the same size run deeper.
+  static constexpr int NS = BK == 64 ? (BM == 64 ? 6 : 3) : (BN == 256 ? 4 : 6);
   static constexpr int DIST = NS - 1;                 // prefetch distance in slices
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_PER_T = BM * 8 / kThreads;  // 16-byte chunks per thread per stage
-  static constexpr int B_PER_T = BN * 8 / kThreads;
+  static constexpr int A_PER_T = BM * CHUNKS / kThreads;  // 16-byte chunks per thread per stage
+  static constexpr int B_PER_T = BN * CHUNKS / kThreads;
   static constexpr int LOADS = A_PER_T + B_PER_T;     // DMA instructions per thread per stage
-  static constexpr int STAGE = (BM + BN) * kRowBytes;
+  static constexpr int STAGE = (BM + BN) * ROWB;
   static constexpr int OUT_PITCH = BN * 2 + 16;      // bytes per staged output row
   static constexpr int OUT_BYTES = BM * OUT_PITCH;
   static constexpr int ROWOFF = OUT_BYTES;           // int64 per row after the staging tile
   static constexpr int LDS = (NS * STAGE > OUT_BYTES + BM * 8) ? NS * STAGE : OUT_BYTES + BM * 8;
-  static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "chunk split");
+  static_assert(BK == 64 || BK == 32, "slice depth");
+  static_assert(BM * CHUNKS % kThreads == 0 && BN * CHUNKS % kThreads == 0, "chunk split");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
-  static_assert(LOADS % 4 == 0, "a slice's DMA instructions split over four blocks");
+  static_assert(LOADS % KS == 0, "a slice's DMA instructions split over its k-steps");
   static_assert(NS * LOADS <= 63, "loads in flight fit the vmcnt counter");
+  static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
+
+// Calls f(integral_constant<I>) ... f(integral_constant<N-1>): the k-steps of a
+// slice, each with its own compile-time part of the slice's loads.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // SIGNAL: the signaling GEMM (reordered stores, counting table, flags); otherwise
 // the plain GEMM with a row-major epilogue.  Separate instantiations keep the
@@ -252,9 +273,10 @@ struct Cfg {
 // physical and each wave's counting table can be read back; every workgroup
 // then runs exactly T iterations, idling through the tile work of a partial
 // last wave.
-template <typename T, int BM, int BN, bool SIGNAL, bool SERIAL>
+template <typename T, int BM, int BN, int BK, bool SIGNAL, bool SERIAL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-  using C = Cfg<BM, BN>;
+  using C = Cfg<BM, BN, BK>;
+  constexpr int kRowBytes = C::ROWB;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // Naming an accumulation register here lets the compiler give the MFMAs
   // their accumulation-register form, so the accumulators live outside the
@@ -271,17 +293,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const int nk = p.K / BK;
   const uint32_t row_bytes = (uint32_t)p.K * 2u;
 
+  // LDS rows hold CHUNKS 16-byte chunks; chunk c of row r is stored at physical
+  // chunk c ^ ((r / WR) % CHUNKS), WR rows filling one 256-byte window of the
+  // 64 banks: the 16 lanes a ds_read_b128 serves per cycle read one logical
+  // chunk of 16 consecutive rows, which this spreads over all 64 banks (BK = 64:
+  // 2 rows per window, XOR over 8 chunks; BK = 32: 4 rows, XOR over 4 chunks).
   // global -> LDS coordinates.  DMA instruction i of wave w fills 1 KiB of
-  // LDS: rows (4 i + w) * 8 .. + 8 of the operand.  Lane l lands at physical
-  // chunk l % 8 of row r = (4 i + w) * 8 + l / 8, which holds the logical
-  // chunk (l % 8) ^ ((r / 2) % 8) = (l % 8) ^ (4 (w % 2) + l / 16); row and
-  // chunk depend on i only through a stride.
-  const uint32_t g_base = (uint32_t)(wave * 8 + (lane >> 3)) * row_bytes +
-                          (uint32_t)(((lane & 7) ^ (4 * (wave & 1) + (lane >> 4))) << 4);
-  const uint32_t g_step = 32u * row_bytes;
+  // LDS: rows (4 i + w) * RPK .. + RPK of the operand.  Lane l lands at
+  // physical chunk l % CHUNKS of row r = (4 i + w) * RPK + l / CHUNKS, which
+  // holds logical chunk (l % CHUNKS) ^ ((r / WR) % CHUNKS); 4 RPK / WR is a
+  // multiple of CHUNKS, so row and chunk depend on i only through a stride.
+  const int dma_row = wave * C::RPK + lane / C::CHUNKS;
+  const uint32_t g_base = (uint32_t)dma_row * row_bytes +
+                          (uint32_t)(((lane % C::CHUNKS) ^ ((dma_row / C::WR) % C::CHUNKS)) << 4);
+  const uint32_t g_step = 4u * C::RPK * row_bytes;
+  static_assert((4 * C::RPK / C::WR) % C::CHUNKS == 0, "the swizzle repeats every 4 RPK rows");
   constexpr uint32_t s_bofs = BM * kRowBytes;      // B rows follow A rows in a stage
   // MFMA fragment reads: row (lane % 32) of each 32-row block, K-chunk ks*2 + lane/32
-  const int frag_row = lane & 31, frag_half = lane >> 5, swz = (lane >> 1) & 7;
+  const int frag_row = lane & 31, frag_half = lane >> 5, swz = (frag_row / C::WR) % C::CHUNKS;
+  static_assert((32 / C::WR) % C::CHUNKS == 0, "every 32-row block has the same swizzle");
   const uint32_t a_frag = (uint32_t)((wm * C::WM + frag_row) * kRowBytes);
   const uint32_t b_frag = (uint32_t)(s_bofs + (wn * C::WN + frag_row) * kRowBytes);
 
@@ -299,17 +329,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     rb = make_rsrc(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K, t.cols * row_bytes);
   };
   // K-slice kt -> LDS stage kt % NS, as C::LOADS DMA instructions per thread;
-  // part p of 4 issues instructions [p * DPB, (p + 1) * DPB)
-  constexpr int DPB = C::LOADS / 4;
+  // part p of KS (one per k-step) issues instructions [p * DPB, (p + 1) * DPB)
+  constexpr int DPB = C::LOADS / C::KS;
   auto stage_dst = [&](int kt) { return smem + (kt % C::NS) * C::STAGE + wave * 1024; };
 #define FO_DMA_PART(PART, KT)                                                                              \
   dma_part<PART, DPB, C::A_PER_T, C::B_PER_T>(ra, rb, stage_dst(KT), s_bofs, g_base, g_step,              \
                                               (uint32_t)(KT) * kRowBytes)
   auto issue = [&](int kt) {
-    FO_DMA_PART(0, kt);
-    FO_DMA_PART(1, kt);
-    FO_DMA_PART(2, kt);
-    FO_DMA_PART(3, kt);
+    static_for<0, C::KS>([&](auto part) { FO_DMA_PART(decltype(part)::value, kt); });
   };
   auto prologue = [&]() {  // slices 0 .. NS-2 of the current tile
 #pragma unroll
@@ -380,67 +407,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     };
 
     // Stage s % NS holds slice s from when it is loaded (during slice s-D, D =
-    // NS-1) until its last fragments are read (third k-step of slice s).
-    // Slice kt+D's loads are spread over the four blocks of slice kt.  Slices
+    // NS-1) until its last fragments are read (k-step KS-1 of slice s).  Slice
+    // kt+D's loads are spread over the KS blocks of slice kt.  Slices
     // 0 .. D-1 were issued ahead (prologue); anything this wave issued before
     // them (the previous tile's stores) is older, so the same counts hold:
     // slice 0 has landed once at most min(D-1, nk-1) slices are in flight.
-    constexpr int D = C::DIST;
+    // Block s of a slice reads the fragments of k-step s+1 while the MFMAs of
+    // k-step s run; the last block hands over to the next slice.
+    constexpr int D = C::DIST, KS = C::KS, LAST = (KS - 1) % 2;
     wait_slices<C::LOADS, D - 1>(nk - 1);
     bare_barrier();
     read_frags(0, 0, 0);
     // The last slice is peeled off so that the loop body has no join point at
     // which the wait-count insertion would have to assume the worst of two paths.
-    auto three_blocks_dma = [&](int kt) {  // and three quarters of slice kt+D's loads
+    auto blocks_dma = [&](int kt) {  // blocks 0 .. KS-2, with parts 0 .. KS-2 of slice kt+D's loads
       __builtin_amdgcn_sched_barrier(0);
-      FO_DMA_PART(0, kt + D);
-      read_frags(1, kt, 1);
-      mfmas(0);
-      block_order_dma();
-      FO_DMA_PART(1, kt + D);
-      read_frags(0, kt, 2);
-      mfmas(1);
-      block_order_dma();
-      FO_DMA_PART(2, kt + D);
-      read_frags(1, kt, 3);
-      mfmas(0);
-      block_order_dma();
+      static_for<0, KS - 1>([&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        FO_DMA_PART(st, kt + D);
+        read_frags((st + 1) % 2, kt, st + 1);
+        mfmas(st % 2);
+        block_order_dma();
+      });
     };
-    auto three_blocks = [&](int kt) {
+    auto blocks = [&](int kt) {
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(1, kt, 1);
-      mfmas(0);
-      block_order();
-      read_frags(0, kt, 2);
-      mfmas(1);
-      block_order();
-      read_frags(1, kt, 3);
-      mfmas(0);
-      block_order();
+      static_for<0, KS - 1>([&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        read_frags((st + 1) % 2, kt, st + 1);
+        mfmas(st % 2);
+        block_order();
+      });
     };
     // Steady state: one path per iteration, so the accumulators keep their
     // registers from one iteration to the next.
     int kt = 0;
     for (; kt + D < nk; ++kt) {
-      three_blocks_dma(kt);
-      FO_DMA_PART(3, kt + D);
+      blocks_dma(kt);
+      FO_DMA_PART(KS - 1, kt + D);
       // this wave's reads of slice kt are complete and its loads of slice kt+1
       // landed (slices kt+2 .. kt+D may still be in flight)
       __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * C::LOADS));
       bare_barrier();  // no wave reads slice kt any more; slice kt+1 is in LDS for every wave
       read_frags(0, kt + 1, 0);
-      mfmas(1);
+      mfmas(LAST);
       block_order();
     }
     // the last handovers: nothing left to load, slices kt+2 .. nk-1 in flight
     auto drain = [&](int kt) {
-      three_blocks(kt);
+      blocks(kt);
       __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
       wait_slices<C::LOADS, D - 2>(nk - 2 - kt);
       bare_barrier();
       read_frags(0, kt + 1, 0);
-      mfmas(1);
+      mfmas(LAST);
       block_order();
     };
     if constexpr (D == 2) {
@@ -448,32 +469,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     } else {
       for (; kt + 1 < nk; ++kt) drain(kt);
     }
-    three_blocks(nk - 1);
-    mfmas(1);
+    blocks(nk - 1);
+    mfmas(LAST);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // all fragment reads done before the staging tile overwrites the ring
 
     // ---- epilogue: destination of every valid row, then the 16-bit tile through LDS
     if (tid < BM) rowoff[tid] = tid < t.rows ? row_offset(p.L, t, b, tid) : 0;
+    // Every LDS address below is one per-thread base plus a compile-time offset
+    // (an instruction immediate), so no per-fragment address is computed once
+    // and kept in a register across tiles: on a 256 x 256 tile that alone ran
+    // the VGPRs out next to 256 accumulators.
+    char *const stage_w = smem + (wm * C::WM + frag_row) * C::OUT_PITCH + (wn * C::WN + frag_half * 4) * 2;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int r = wm * C::WM + i * 32 + frag_row;
-          const int c = wn * C::WN + j * 32 + g4 * 8 + frag_half * 4;
           const f32x4 v = {acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1], acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]};
-          *reinterpret_cast<u32x2 *>(smem + r * C::OUT_PITCH + c * 2) = pack4<T>(v);
+          *reinterpret_cast<u32x2 *>(stage_w + i * 32 * C::OUT_PITCH + (j * 32 + g4 * 8) * 2) = pack4<T>(v);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     __syncthreads();
-    constexpr int CPR = BN / 8;  // 16-byte chunks per row
+    constexpr int CPR = BN / 8;                 // 16-byte chunks per row
+    constexpr int RPI = kThreads / CPR;         // rows per iteration of the store loop
+    static_assert(kThreads % CPR == 0, "whole rows per iteration");
+    const int r_t = tid / CPR, c8 = tid % CPR;  // a thread's row in each block of RPI rows, and its chunk
+    const char *const stage_r = smem + r_t * C::OUT_PITCH + c8 * 16;
+    const int64_t *const rowoff_t = rowoff + r_t;
+    const bool col_ok = c8 * 8 < t.cols;
 #pragma unroll
-    for (int i = 0; i < BM * CPR / kThreads; ++i) {
-      const int q = tid + i * kThreads, r = q / CPR, c8 = q % CPR;
-      if (r < t.rows && c8 * 8 < t.cols) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * C::OUT_PITCH + c8 * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(v, rc, (uint32_t)rowoff[r] * 2u + (uint32_t)c8 * 16u, 0, kStoreSys);
+    for (int i = 0; i < BM / RPI; ++i) {
+      if (r_t + i * RPI < t.rows && col_ok) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage_r + i * RPI * C::OUT_PITCH);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, (uint32_t)rowoff_t[i * RPI] * 2u + (uint32_t)c8 * 16u, 0,
+                                               kStoreSys);
       }
     }
 
@@ -520,10 +552,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #undef FO_DMA_PART
 }
 
-template <typename T, int BM, int BN, bool SIGNAL, bool SERIAL>
+template <typename T, int BM, int BN, int BK, bool SIGNAL, bool SERIAL>
 int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
-  using C = Cfg<BM, BN>;
-  const void *fn = reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, SIGNAL, SERIAL>);
+  using C = Cfg<BM, BN, BK>;
+  const void *fn = reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, SIGNAL, SERIAL>);
   static bool configured = false;  // per process; the attribute is per kernel and device-independent
   if (!configured) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess) return FO_ERR_HIP;
@@ -539,16 +571,17 @@ int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
     if (hipLaunchCooperativeKernel(fn, dim3(gp.W), dim3(kThreads), args, C::LDS, s) != hipSuccess) return FO_ERR_HIP;
     return FO_OK;
   } else {
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, SIGNAL, false>), dim3(gp.W), dim3(kThreads), C::LDS, s, gp);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, SIGNAL, false>), dim3(gp.W), dim3(kThreads), C::LDS, s, gp);
     return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
   }
 }
 
 template <typename T, bool SIGNAL, bool SERIAL>
 int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
-  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, SIGNAL, SERIAL>(p, gp, s);
-  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, SIGNAL, SERIAL>(p, gp, s);
-  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 256 && p->BN == 256) return launch_typed<T, 256, 256, 32, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, 64, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, 64, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, 64, SIGNAL, SERIAL>(p, gp, s);
   return FO_ERR_UNSUPPORTED;
 }
 

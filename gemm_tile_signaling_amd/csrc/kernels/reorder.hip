@@ -235,7 +235,10 @@ __global__ __launch_bounds__(kThreads) void row_exchange_kernel(ExchangeParams p
 
 template <typename T, int ACT, bool BIAS>
 void launch_post_ep_typed(const fo_plan *p, const ReorderParams &rp, hipStream_t s) {
-  if (p->BN == 128)
+  if (p->BN == 256)
+    hipLaunchKernelGGL((post_ep_kernel<T, 64, 32, ACT, BIAS>), dim3(p->NT, (p->BM + 63) / 64), dim3(kThreads), 0, s,
+                       rp);
+  else if (p->BN == 128)
     hipLaunchKernelGGL((post_ep_kernel<T, 128, 16, ACT, BIAS>), dim3(p->NT, (p->BM + 127) / 128), dim3(kThreads), 0,
                        s, rp);
   else
@@ -259,7 +262,10 @@ void launch_post_ep_act(const fo_plan *p, const ReorderParams &rp, int act, hipS
 }
 
 int launch_reorder_params(const fo_plan *p, const ReorderParams &rp, int32_t nslots, hipStream_t s) {
-  if (p->BN == 128) {
+  if (p->BN == 256) {
+    constexpr int RPB = 64;
+    hipLaunchKernelGGL((reorder_kernel<RPB, 32>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
+  } else if (p->BN == 128) {
     constexpr int RPB = 128;
     hipLaunchKernelGGL((reorder_kernel<RPB, 16>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
   } else if (p->BN == 64) {
@@ -292,7 +298,7 @@ void launch_exchange_typed(const ExchangeParams &ep, int act, dim3 grid, hipStre
 
 int launch_post_ep(const fo_plan *p, const void *src, void *dst, const void *bias, int act, hipStream_t s) {
   if (p->NT == 0) return FO_OK;
-  if (p->BN != 128 && p->BN != 64) return FO_ERR_UNSUPPORTED;
+  if (p->BN != 256 && p->BN != 128 && p->BN != 64) return FO_ERR_UNSUPPORTED;
   ReorderParams rp{};
   rp.src = static_cast<const uint16_t *>(src);
   rp.dst = static_cast<uint16_t *>(dst);

@@ -17,7 +17,7 @@
 namespace {
 
 bool valid_tile(int32_t BM, int32_t BN) {
-  return (BM == 256 && BN == 128) || (BM == 128 && BN == 128) || (BM == 64 && BN == 64);
+  return (BM == 256 && BN == 256) || (BM == 256 && BN == 128) || (BM == 128 && BN == 128) || (BM == 64 && BN == 64);
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -118,7 +118,7 @@ typedef struct fo_plan_desc {
                                       tile's operand rows fit 32-bit byte offsets:
                                       max(BM, BN) * K * 2 < 2^32 (K < 2^23 at BM = 256)       */
   int32_t dtype;                   /* fo_dtype                                                */
-  int32_t BM, BN;                  /* tile: 256x128, 128x128 or 64x64; 0,0 = 256x128          */
+  int32_t BM, BN;                  /* tile: 256x256, 256x128, 128x128 or 64x64; 0,0 = 256x128 */
   int32_t swizzle;                 /* S >= 1; 0 = 4                                           */
   int32_t wave_size;               /* W >= 1; 0 = the device's CU count (256 if host-only)    */
   int32_t num_groups;              /* P; 0 = one wave per group (waves_per_group ignored)     */
