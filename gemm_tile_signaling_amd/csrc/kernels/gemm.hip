@@ -15,8 +15,13 @@
 //     of positions of the wave, so the tiles sharing an XCD's L2 are
 //     neighbours in the swizzled order.  This only permutes workgroups
 //     inside a wave.
-//   * 256 threads = 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2)
-//     sub-tile made of 32 x 32 blocks computed with v_mfma_f32_32x32x16.
+//   * 4 waves in a 2 x 2 grid, one per SIMD, each owning a (BM/2) x (BN/2)
+//     sub-tile; the 256 x 128 tile runs 8 waves in a 4 x 2 grid instead, two
+//     per SIMD with a 64 x 64 sub-tile each (200 registers a wave), so that
+//     while one wave waits on its LDS reads or the slice barrier the other
+//     keeps the matrix pipe busy, and 112 registers per SIMD stay free for
+//     the consumer's waves.  Sub-tiles are made of 32 x 32 blocks computed
+//     with v_mfma_f32_32x32x16.
 //     A and B fragments are passed to the MFMA swapped (B as the first
 //     operand) so that every lane ends up with 4 consecutive columns of one
 //     output row, which the epilogue writes as 8-byte pieces.
@@ -79,7 +84,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kThreads = 256;
 constexpr int kVmcntZero = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 constexpr int kLgkmcntZero = 0xC07F;            // s_waitcnt lgkmcnt(0), other counters unconstrained
 // Cache policy of the output stores: system scope (sc0 | sc1), i.e. written
@@ -128,19 +132,21 @@ __device__ __forceinline__ f32x16 mma<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
                                                 0, 0);
 }
 
-// Part PART of a K-slice's LDS-DMA loads: DPB consecutive instructions of the
-// thread's A_PER_T (A rows) then B_PER_T (B rows).  Lane l of instruction q
-// lands at LDS offset dst + q' * 4096 + 16 l of its operand's region.
-template <int PART, int DPB, int A_PER_T, int B_PER_T>
+// Part PART of a K-slice's LDS-DMA loads: up to DPB consecutive instructions
+// of the thread's A_PER_T (A rows) then B_PER_T (B rows).  Lane l of
+// instruction q lands at LDS offset dst + q' * NW KiB + 16 l of its operand's
+// region (NW waves per workgroup, each wave 1 KiB of every instruction).
+template <int PART, int DPB, int A_PER_T, int B_PER_T, int NW>
 __device__ __forceinline__ void dma_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, char *dst,
                                          uint32_t b_region, uint32_t g_base, uint32_t g_step, uint32_t soff) {
-  constexpr int q0 = PART * DPB, q1 = q0 + DPB;
+  constexpr int q0 = PART * DPB, q1 = q0 + DPB < A_PER_T + B_PER_T ? q0 + DPB : A_PER_T + B_PER_T;
 #pragma unroll
   for (int q = q0; q < (q1 < A_PER_T ? q1 : A_PER_T); ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(dst + q * 4096), 16, g_base + q * g_step, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(dst + q * NW * 1024), 16, g_base + q * g_step, soff,
+                                             0, 0);
 #pragma unroll
   for (int q = (q0 > A_PER_T ? q0 : A_PER_T); q < q1; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(dst + b_region + (q - A_PER_T) * 4096), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(dst + b_region + (q - A_PER_T) * NW * 1024), 16,
                                              g_base + (q - A_PER_T) * g_step, soff, 0, 0);
 }
 
@@ -216,7 +222,7 @@ __device__ __forceinline__ bool wave_snapshot(const GemmParams &p, int w) {
   if (!grid_barrier(bar, status, 2u * w, p.timeout_ticks)) return false;
   if (blockIdx.x == 0) {
     uint32_t *snap = p.serial + 2 * (int64_t)w * p.P;
-    for (int i = threadIdx.x; i < p.P; i += kThreads) {
+    for (int i = threadIdx.x; i < p.P; i += blockDim.x) {
       snap[i] = __hip_atomic_load(&p.cnt[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       snap[p.P + i] = __hip_atomic_load(&p.flag[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -224,9 +230,13 @@ __device__ __forceinline__ bool wave_snapshot(const GemmParams &p, int w) {
   return grid_barrier(bar, status, 2u * w + 1u, p.timeout_ticks);
 }
 
-// Tile BM x BN, K-slices of BK (64 or 32) staged in LDS.
-template <int BM, int BN, int BK>
+// Tile BM x BN, K-slices of BK (64 or 32) staged in LDS, NW waves per
+// workgroup (4: one per SIMD; 8: two per SIMD) in a WGM x WGN grid.
+template <int BM, int BN, int BK, int NW>
 struct Cfg {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WGM = NW == 4 ? 2 : (BM == BN ? 2 : 4);
+  static constexpr int WGN = NW / WGM;
   static constexpr int ROWB = BK * 2;                 // bytes of one staged row of A or B
   static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per staged row
   static constexpr int KS = BK / 16;                  // MFMA k-steps per slice
@@ -237,20 +247,21 @@ struct Cfg {
   // half-depth slices (BK = 32) let a ring of the same size run deeper.
   static constexpr int NS = BK == 64 ? (BM == 64 ? 6 : 3) : (BN == 256 ? 4 : 6);
   static constexpr int DIST = NS - 1;                 // prefetch distance in slices
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_PER_T = BM * CHUNKS / kThreads;  // 16-byte chunks per thread per stage
-  static constexpr int B_PER_T = BN * CHUNKS / kThreads;
+  static constexpr int A_PER_T = BM * CHUNKS / THREADS;  // 16-byte chunks per thread per stage
+  static constexpr int B_PER_T = BN * CHUNKS / THREADS;
   static constexpr int LOADS = A_PER_T + B_PER_T;     // DMA instructions per thread per stage
+  static constexpr int DPB = (LOADS + KS - 1) / KS;   // of them issued per k-step (fewer in the last parts)
   static constexpr int STAGE = (BM + BN) * ROWB;
   static constexpr int OUT_PITCH = BN * 2 + 16;      // bytes per staged output row
   static constexpr int OUT_BYTES = BM * OUT_PITCH;
   static constexpr int ROWOFF = OUT_BYTES;           // int64 per row after the staging tile
   static constexpr int LDS = (NS * STAGE > OUT_BYTES + BM * 8) ? NS * STAGE : OUT_BYTES + BM * 8;
   static_assert(BK == 64 || BK == 32, "slice depth");
-  static_assert(BM * CHUNKS % kThreads == 0 && BN * CHUNKS % kThreads == 0, "chunk split");
-  static_assert(FM >= 1 && FN >= 1, "wave tile");
-  static_assert(LOADS % KS == 0, "a slice's DMA instructions split over its k-steps");
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(BM * CHUNKS % THREADS == 0 && BN * CHUNKS % THREADS == 0, "chunk split");
+  static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(NS * LOADS <= 63, "loads in flight fit the vmcnt counter");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
@@ -273,9 +284,9 @@ __device__ __forceinline__ void static_for(F &&f) {
 // physical and each wave's counting table can be read back; every workgroup
 // then runs exactly T iterations, idling through the tile work of a partial
 // last wave.
-template <typename T, int BM, int BN, int BK, bool SIGNAL, bool SERIAL>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-  using C = Cfg<BM, BN, BK>;
+template <typename T, int BM, int BN, int BK, int NW, bool SIGNAL, bool SERIAL>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
+  using C = Cfg<BM, BN, BK, NW>;
   constexpr int kRowBytes = C::ROWB;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // Naming an accumulation register here lets the compiler give the MFMAs
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations go to M0
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int g = blockIdx.x;
   const int pos = p.remap ? (g & 7) * (p.W >> 3) + (g >> 3) : g;
   const int nk = p.K / BK;
@@ -299,15 +310,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   // chunk of 16 consecutive rows, which this spreads over all 64 banks (BK = 64:
   // 2 rows per window, XOR over 8 chunks; BK = 32: 4 rows, XOR over 4 chunks).
   // global -> LDS coordinates.  DMA instruction i of wave w fills 1 KiB of
-  // LDS: rows (4 i + w) * RPK .. + RPK of the operand.  Lane l lands at
-  // physical chunk l % CHUNKS of row r = (4 i + w) * RPK + l / CHUNKS, which
-  // holds logical chunk (l % CHUNKS) ^ ((r / WR) % CHUNKS); 4 RPK / WR is a
+  // LDS: rows (NW i + w) * RPK .. + RPK of the operand.  Lane l lands at
+  // physical chunk l % CHUNKS of row r = (NW i + w) * RPK + l / CHUNKS, which
+  // holds logical chunk (l % CHUNKS) ^ ((r / WR) % CHUNKS); NW RPK / WR is a
   // multiple of CHUNKS, so row and chunk depend on i only through a stride.
   const int dma_row = wave * C::RPK + lane / C::CHUNKS;
   const uint32_t g_base = (uint32_t)dma_row * row_bytes +
                           (uint32_t)(((lane % C::CHUNKS) ^ ((dma_row / C::WR) % C::CHUNKS)) << 4);
-  const uint32_t g_step = 4u * C::RPK * row_bytes;
-  static_assert((4 * C::RPK / C::WR) % C::CHUNKS == 0, "the swizzle repeats every 4 RPK rows");
+  const uint32_t g_step = (uint32_t)NW * C::RPK * row_bytes;
+  static_assert((NW * C::RPK / C::WR) % C::CHUNKS == 0, "the swizzle repeats every NW RPK rows");
   constexpr uint32_t s_bofs = BM * kRowBytes;      // B rows follow A rows in a stage
   // MFMA fragment reads: row (lane % 32) of each 32-row block, K-chunk ks*2 + lane/32
   const int frag_row = lane & 31, frag_half = lane >> 5, swz = (frag_row / C::WR) % C::CHUNKS;
@@ -330,11 +341,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   };
   // K-slice kt -> LDS stage kt % NS, as C::LOADS DMA instructions per thread;
   // part p of KS (one per k-step) issues instructions [p * DPB, (p + 1) * DPB)
-  constexpr int DPB = C::LOADS / C::KS;
+  constexpr int DPB = C::DPB;
   auto stage_dst = [&](int kt) { return smem + (kt % C::NS) * C::STAGE + wave * 1024; };
 #define FO_DMA_PART(PART, KT)                                                                              \
-  dma_part<PART, DPB, C::A_PER_T, C::B_PER_T>(ra, rb, stage_dst(KT), s_bofs, g_base, g_step,              \
-                                              (uint32_t)(KT) * kRowBytes)
+  dma_part<PART, DPB, C::A_PER_T, C::B_PER_T, NW>(ra, rb, stage_dst(KT), s_bofs, g_base, g_step,          \
+                                                  (uint32_t)(KT) * kRowBytes)
   auto issue = [&](int kt) {
     static_for<0, C::KS>([&](auto part) { FO_DMA_PART(decltype(part)::value, kt); });
   };
@@ -385,14 +396,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // alternating with its MFMAs, so the wave never sits on a queue while the
     // matrix pipe has nothing to do.
     constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
-    auto block_order_dma = [&]() {
+    auto block_order_dma = [&](auto nd) {  // nd: this block's DMA instructions
+      constexpr int ND = decltype(nd)::value;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        if (r % 2 == 0 && r / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                 // DS read
-        if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+        if (r % 2 == 0 && r / 2 < ND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                // DS read
+        if (r < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
       }
-      if ((NR + 1) / 2 < DPB) __builtin_amdgcn_sched_group_barrier(0x020, DPB - (NR + 1) / 2, 0);
+      if ((NR + 1) / 2 < ND) __builtin_amdgcn_sched_group_barrier(0x020, ND - (NR + 1) / 2, 0);
       if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -424,10 +436,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, KS - 1>([&](auto sc) {
         constexpr int st = decltype(sc)::value;
+        constexpr int left = C::LOADS - st * DPB;
         FO_DMA_PART(st, kt + D);
         read_frags((st + 1) % 2, kt, st + 1);
         mfmas(st % 2);
-        block_order_dma();
+        block_order_dma(std::integral_constant<int, (left < 0 ? 0 : left < DPB ? left : DPB)>{});
       });
     };
     auto blocks = [&](int kt) {
@@ -494,8 +507,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       }
     __syncthreads();
     constexpr int CPR = BN / 8;                 // 16-byte chunks per row
-    constexpr int RPI = kThreads / CPR;         // rows per iteration of the store loop
-    static_assert(kThreads % CPR == 0, "whole rows per iteration");
+    constexpr int RPI = C::THREADS / CPR;       // rows per iteration of the store loop
+    static_assert(C::THREADS % CPR == 0 && BM % RPI == 0, "whole rows per iteration");
     const int r_t = tid / CPR, c8 = tid % CPR;  // a thread's row in each block of RPI rows, and its chunk
     const char *const stage_r = smem + r_t * C::OUT_PITCH + c8 * 16;
     const int64_t *const rowoff_t = rowoff + r_t;
@@ -552,10 +565,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #undef FO_DMA_PART
 }
 
-template <typename T, int BM, int BN, int BK, bool SIGNAL, bool SERIAL>
+template <typename T, int BM, int BN, int BK, int NW, bool SIGNAL, bool SERIAL>
 int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
-  using C = Cfg<BM, BN, BK>;
-  const void *fn = reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, SIGNAL, SERIAL>);
+  using C = Cfg<BM, BN, BK, NW>;
+  const void *fn = reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, NW, SIGNAL, SERIAL>);
   static bool configured = false;  // per process; the attribute is per kernel and device-independent
   if (!configured) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess) return FO_ERR_HIP;
@@ -564,24 +577,26 @@ int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
   if constexpr (SERIAL) {
     // every workgroup must be resident at once, or the barriers could not complete
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, C::LDS) != hipSuccess) return FO_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, C::THREADS, C::LDS) != hipSuccess)
+      return FO_ERR_HIP;
     if ((int64_t)per_cu * pl->num_cus < gp.W) return FO_ERR_UNSUPPORTED;
     GemmParams arg = gp;
     void *args[] = {&arg};
-    if (hipLaunchCooperativeKernel(fn, dim3(gp.W), dim3(kThreads), args, C::LDS, s) != hipSuccess) return FO_ERR_HIP;
+    if (hipLaunchCooperativeKernel(fn, dim3(gp.W), dim3(C::THREADS), args, C::LDS, s) != hipSuccess)
+      return FO_ERR_HIP;
     return FO_OK;
   } else {
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, SIGNAL, false>), dim3(gp.W), dim3(kThreads), C::LDS, s, gp);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, NW, SIGNAL, false>), dim3(gp.W), dim3(C::THREADS), C::LDS, s, gp);
     return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
   }
 }
 
 template <typename T, bool SIGNAL, bool SERIAL>
 int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
-  if (p->BM == 256 && p->BN == 256) return launch_typed<T, 256, 256, 32, SIGNAL, SERIAL>(p, gp, s);
-  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, 64, SIGNAL, SERIAL>(p, gp, s);
-  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, 64, SIGNAL, SERIAL>(p, gp, s);
-  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, 64, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 256 && p->BN == 256) return launch_typed<T, 256, 256, 32, 4, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, 64, 8, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, 64, 4, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, 64, 4, SIGNAL, SERIAL>(p, gp, s);
   return FO_ERR_UNSUPPORTED;
 }
 

@@ -323,13 +323,18 @@ int fo_gemm_plain(const fo_plan *plan, const void *A, const void *B, void *C, hi
  * num_workgroups: persistent grid size, 0 = the device's CU count; at most
  *      the CU count, else FO_ERR_INVALID.  Residency: the consumer's
  *      workgroups wait on the CUs for flags that the GEMM raises, so the GEMM's
- *      W workgroups must still find room beside them.  A GEMM workgroup holds
- *      up to 376 of a SIMD's 512 registers per lane and 144 KiB of the CU's
- *      160 KiB LDS; a consumer workgroup is one wave per SIMD of at most 96
- *      registers and no LDS to speak of, so one consumer workgroup per CU fits
- *      beside the GEMM and two do not: a grid above the CU count could keep
- *      GEMM workgroups from being dispatched until the consumer times out.
- *      fo_consume_group_gated has no such condition.
+ *      W workgroups must still find room beside them.  A GEMM workgroup of the
+ *      64x64, 128x128 or 256x128 tile holds up to 408 of a SIMD's 512
+ *      registers per lane (two 204-register waves on 256x128) and 144 KiB of
+ *      the CU's 160 KiB LDS; a consumer workgroup is one wave per SIMD of at
+ *      most 96 registers and no LDS to speak of, so one consumer workgroup per
+ *      CU fits beside the GEMM and two do not: a grid above the CU count could
+ *      keep GEMM workgroups from being dispatched until the consumer times
+ *      out.  A 256x256 workgroup takes all 512 registers, so nothing fits
+ *      beside it: do not pair this consumer with that tile.
+ *      fo_consume_group_gated has no such condition (with the 256x256 tile a
+ *      stream-wait wave dispatched ahead of the GEMM still delays one GEMM
+ *      workgroup until another one ends: correct, but slow).
  * timeout_us: upper bound on any one wait (0 = 2 s).  A workgroup that
  *      waits longer stores FO_ERR_TIMEOUT into *dev_status (if it was still
  *      0) and every workgroup then stops; later spans are left untouched.
