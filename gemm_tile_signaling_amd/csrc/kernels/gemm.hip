@@ -56,14 +56,14 @@
 //     once into LDS; then 16-byte coalesced buffer stores, written through
 //     the L2 (system-scope cache policy).  Once every wave has read
 //     the staging tile, the workgroup issues the next tile's first two
-//     K-slices.  With signaling on, each wave then waits for its own stores
-//     to complete (the younger loads stay in flight), the workgroup meets at
-//     a barrier, and one lane releases the tile to device scope and
-//     increments cnt[group]; the lane that brings it to epoch * |G_group|
-//     stores flag[group] = epoch with release semantics.  The signal's waits
-//     thus overlap the next tile's first loads.  With epoch stamps on, that
-//     lane also stores the epoch into the slot's stamp just before the
-//     release, so a consumer can check what the release made visible.
+//     K-slices.  With signaling on, each wave then waits for all its memory
+//     operations to complete (the tile's stores were written through the L2,
+//     so complete means visible to device-coherent loads), the workgroup
+//     meets at a barrier, and one lane increments cnt[group]; the lane that
+//     brings it to epoch * |G_group| stores flag[group] = epoch with release
+//     semantics.  The signal's waits thus overlap the next tile's first
+//     loads.  With epoch stamps on, that lane first stores the epoch into the
+//     slot's stamp the same way, so a consumer can check what it was shown.
 //   * A third instantiation serializes the waves for tests and traces (a
 //     device-wide barrier and a snapshot of the signal words after every
 //     wave, cooperative launch); the hot path never runs it.
@@ -87,9 +87,10 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 constexpr int kVmcntZero = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 constexpr int kLgkmcntZero = 0xC07F;            // s_waitcnt lgkmcnt(0), other counters unconstrained
 // Cache policy of the output stores: system scope (sc0 | sc1), i.e. written
-// through the L2, so the agent-scope release before a tile is counted finds
-// next to nothing left to write back (2-6% faster signaling GEMM on the
-// shapes with short K, where the release is a larger share of a tile).
+// through the L2 to the device's point of coherence.  A finished tile is then
+// visible on every XCD once its stores are complete, so it is counted without
+// an L2 write-back (which cost 5-9% of the signaling GEMM on the shapes with
+// short K, one per tile).
 constexpr int kStoreSys = 0x11;
 
 // s_waitcnt immediate for vmcnt(n) with the other counters unconstrained (gfx9 encoding)
@@ -532,21 +533,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
       prologue();
     }
 
-    // ---- signal: counting table, then the group's flag.  Each wave waits
-    // until its own tile stores are complete (the loads just issued may stay
-    // in flight: they are younger); after the barrier one lane releases the
-    // whole workgroup's stores to device scope (a single L2 write-back per
-    // tile) before it counts the tile.
+    // ---- signal: counting table, then the group's flag.  The tile's stores
+    // went out with the system-scope cache policy, i.e. written through the
+    // L2 to the device's point of coherence, and such a store counts as
+    // complete only once the memory side has taken it.  So each wave waits
+    // until every memory operation it issued is complete (its stores, and the
+    // next tile's first slices issued after them: the ISA does not order a
+    // store's completion with younger loads), the workgroup meets at a
+    // barrier, and the whole tile is then visible to device-coherent loads on
+    // every XCD without an L2 write-back.  One lane counts the tile; the lane
+    // that completes the group raises the flag with a release store.
     if constexpr (SIGNAL) {
-      if (!more)
-        __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      else  // the next tile's min(D, nk) slices were issued after the stores
-        wait_slices<C::LOADS, C::DIST>(nk);
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
       __syncthreads();
       if (tid == 0) {
-        // the stamp is released together with the tile's stores
-        if (p.stamps) __hip_atomic_store(&p.stamps[b], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (p.stamps) {  // device scope, written through like the tile; complete before the tile is counted
+          __hip_atomic_store(&p.stamps[b], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        }
         const uint32_t old = __hip_atomic_fetch_add(&p.cnt[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool fire = old + 1u == p.fire_mult * (uint32_t)p.thr[grp];
         if (fire) __hip_atomic_store(&p.flag[grp], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);

@@ -84,14 +84,15 @@ typedef enum fo_b_layout {
 #define FO_PLAN_HOST_ONLY 0x1u   /* build the tables on the host only; enqueue calls reject the plan */
 #define FO_PLAN_EPOCH_STAMPS 0x2u /* stale-read detector: the signal buffer grows by one word per
                                     slot (stamp_offset, fo_plan_info); the signaling GEMM writes the
-                                    epoch into its tile's stamp after the tile's stores and before
-                                    the release that precedes the count, and the consumer, after a
+                                    epoch into its tile's stamp after the tile's stores are complete
+                                    and before the tile is counted, and the consumer, after a
                                     group's signal, reads every stamp of the group with the same
                                     loads it uses for the span: a stamp of an older epoch means the
                                     signal did not make the tile's writes visible, and it stores
                                     FO_ERR_STALE into its status word (it still finishes the
-                                    group).  The stamps rely on the same device-scope release as
-                                    the data, so they observe the protocol, not just the data   */
+                                    group).  The stamps are published the same way as the data
+                                    (written through the L2 and complete before the count), so
+                                    they observe the protocol, not just the data               */
 
 /*
  * Problem description.  C[M, N] = A[M, K] . B^T where B is stored [N, K]
@@ -240,10 +241,11 @@ int fo_plan_search(const fo_plan *plan, double gemm_seconds, const double *curve
 /*
  * Signaling GEMM (deep-dive 五 › 扩展主循环 and Epilogue 集成): C = A . B^T
  * with every finished tile stored through the mapping table into
- * `reorder_buf` (M*N elements, the contiguous per-group spans), followed by
- * a release of the tile's stores to device scope, one atomic increment of
- * cnt[group], and -- by the tile that brings cnt[group] to epoch*|G_group|
- * -- a release store flag[group] = epoch.
+ * `reorder_buf` (M*N elements, the contiguous per-group spans) with
+ * stores written through the L2 to the device's point of coherence; once
+ * every one of them is complete, one atomic increment of cnt[group], and --
+ * by the tile that brings cnt[group] to epoch*|G_group| -- a release store
+ * flag[group] = epoch.
  *
  * sig: device uint32[sig_words] (fo_plan_info): the counting table cnt[P] at
  *      word 0 and the flags flag[P] at word flag_offset, the first multiple of
