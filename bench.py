@@ -12,8 +12,9 @@ waves).  Schedules: partitions (2) and (1, 1), the consumer gated in the
 stream's queue or polling on the CUs, the post-reorder whole or group by
 group.  The schedule is chosen from interleaved blocks; then, five times,
 W warm-up passes and exactly K timed passes (synchronised on both sides,
-host clock, with device events around the region); ``value`` is useful GEMM
-TFLOP/s of the whole step (2 M N K per step / step time) of the median
+host clock, with device events around the region, and every fourth GEMM
+bracketed by events on its own stream for the roofline); ``value`` is useful
+GEMM TFLOP/s of the whole step (2 M N K per step / step time) of the median
 region.
 
 Prints one JSON line.  Extra fields: the signaling and plain GEMMs measured
@@ -40,6 +41,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+# In the timed regions (and the choice blocks) every EV_EVERY-th pass brackets its GEMM with an event pair
+# on the GEMM's stream for the roofline: a pair in front of every GEMM delays each pass by 4-5 us.
+EV_EVERY = 4
 
 
 def _args():
@@ -319,31 +323,6 @@ def committed_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the GEMM kernel's sources and build flags: ties committed traffic counters to the code they measured."""
-    import hashlib
-    h = hashlib.sha256()
-    for rel in ("gemm_tile_signaling_amd/csrc/kernels/gemm.hip", "gemm_tile_signaling_amd/csrc/kernels/buffer.h",
-                "gemm_tile_signaling_amd/csrc/fo_internal.h", "gemm_tile_signaling_amd/build.py"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
-def committed_traffic(workload: str):
-    """HBM bytes per launch of the signaling GEMM from the committed rocprofv3 counter passes, or None
-    when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"signal_gemm_{workload}_traffic.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
-
-
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -493,8 +472,8 @@ def main():
         torch.cuda.synchronize()
         check(pipe)
 
-    # choose the schedule: blocks of K passes (each GEMM bracketed by events, as in the timed
-    # region), every schedule in turn, three rounds, so that clock and power drift falls on all of
+    # choose the schedule: blocks of K passes (every EV_EVERY-th GEMM bracketed by events, as in the
+    # timed region), every schedule in turn, three rounds, so that clock and power drift falls on all of
     # them alike; the serial schedule (GEMM, consumer, post-reorder on one queue) is measured alike
     passes(scheds[0]["pipe"], a.warmup)
     order = [(i, False) for i in range(len(scheds))] + [(0, True)]
@@ -505,7 +484,7 @@ def main():
             passes(pipe, 5, serial=serial)
             t0 = time.perf_counter()
             for j in range(a.steps):
-                pipe.step(events={"gemm": pick_ev[j]}, serial=serial)
+                pipe.step(events={"gemm": pick_ev[j]} if j % EV_EVERY == 0 else None, serial=serial)
             pipe.join()
             torch.cuda.synchronize()
             picks[(i, serial)].append((time.perf_counter() - t0) * 1e3 / a.steps)
@@ -519,8 +498,8 @@ def main():
 
     # timed: five regions, each W warm-up passes then exactly K passes of the chosen schedule,
     # synchronised on both sides; a device event pair brackets each region (first GEMM's start to
-    # the last post-reorder's end) beside the host clock; the GEMM of every pass is bracketed by
-    # events on its own stream for the roofline.  The value is the median region.  Before the
+    # the last post-reorder's end) beside the host clock; the GEMM of every EV_EVERY-th pass is
+    # bracketed by events on its own stream for the roofline.  The value is the median region.  Before the
     # first region the chosen schedule runs 100 untimed passes, so no region starts in a clock ramp.
     passes(pipe, 100)
     reg = []
@@ -530,14 +509,14 @@ def main():
         t0 = time.perf_counter()
         region_ev[r][0].record(pipe.next_gemm_stream())
         for i in range(a.steps):
-            pipe.step(events={"gemm": gemm_ev[r][i]})
+            pipe.step(events={"gemm": gemm_ev[r][i]} if i % EV_EVERY == 0 else None)
         region_ev[r][1].record(pipe.post_stream)
         pipe.join()
         torch.cuda.synchronize()
         host_ms = (time.perf_counter() - t0) * 1e3 / a.steps
         launches[0] += a.steps
         check(pipe)
-        each = [s.elapsed_time(e) for s, e in gemm_ev[r]]
+        each = [s.elapsed_time(e) for i, (s, e) in enumerate(gemm_ev[r]) if i % EV_EVERY == 0]
         dev_ms = region_ev[r][0].elapsed_time(region_ev[r][1]) / a.steps
         reg.append(dict(host_ms=host_ms, device_ms=dev_ms, gemm_ms=float(np.mean(each)),
                         gemm_q=np.percentile(each, [10, 50, 90]).tolist(), launches=[first, launches[0]]))
@@ -638,7 +617,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(w.name),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes": 2 * (w.M * w.K + w.N * w.K + w.M * w.N),
-                     "kernel": "signaling GEMM inside the timed passes (events on its own stream)"},
+                     "kernel": "signaling GEMM inside the timed passes (events on its own stream, every %d-th pass)" % EV_EVERY},
         "timed_regions": [{"host_ms_per_step": round(r["host_ms"], 4), "device_ms_per_step": round(r["device_ms"], 4),
                            "signal_gemm_ms": round(r["gemm_ms"], 4)} for r in reg],
         "timed_region_used": mid,
