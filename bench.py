@@ -12,8 +12,8 @@ waves).  Schedules: partitions (2) and (1, 1), the consumer gated in the
 stream's queue or polling on the CUs, the post-reorder whole or group by
 group.  The schedule is chosen from interleaved blocks; then, five times,
 W warm-up passes and exactly K timed passes (synchronised on both sides,
-host clock, with device events around the region, and every fourth GEMM
-bracketed by events on its own stream for the roofline); ``value`` is useful
+host clock, with device events around the region, and every GEMM bracketed
+by events on its own stream for the roofline); ``value`` is useful
 GEMM TFLOP/s of the whole step (2 M N K per step / step time) of the median
 region.
 
@@ -41,9 +41,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
-# In the timed regions (and the choice blocks) every EV_EVERY-th pass brackets its GEMM with an event pair
-# on the GEMM's stream for the roofline: a pair in front of every GEMM delays each pass by 4-5 us.
-EV_EVERY = 4
 
 
 def _args():
@@ -64,8 +61,46 @@ def _args():
     return ap.parse_args()
 
 
+class _HipEvent:
+    """A HIP event for timing on a given stream, created with hipEventDisableSystemFence: recording it does
+    no system-scope memory fence (which only matters to a host reading device memory right after the event;
+    every read here follows a device synchronisation).  Recording a torch event, which does the fence, in
+    front of each GEMM delayed every pass by about 4.5 us; this one by about 0.3 us."""
+    _lib = None
+    _live = []
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if _HipEvent._lib is None:
+            _HipEvent._lib = ctypes.CDLL("libamdhip64.so")
+        self._c = ctypes
+        self.h = ctypes.c_void_p()
+        if _HipEvent._lib.hipEventCreateWithFlags(ctypes.byref(self.h), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        _HipEvent._live.append(self)
+
+    def record(self, stream=None):
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream()
+        if _HipEvent._lib.hipEventRecord(self.h, self._c.c_void_p(int(st.cuda_stream))):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        ms = self._c.c_float()
+        if _HipEvent._lib.hipEventElapsedTime(self._c.byref(ms), self.h, end.h):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    @classmethod
+    def destroy_all(cls):
+        for e in cls._live:
+            cls._lib.hipEventDestroy(e.h)
+        cls._live = []
+
+
 def _event_pairs(torch, n):
-    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    return [(_HipEvent(), _HipEvent()) for _ in range(n)]
 
 
 def _flush_mall(torch, scratch):
@@ -472,8 +507,8 @@ def main():
         torch.cuda.synchronize()
         check(pipe)
 
-    # choose the schedule: blocks of K passes (every EV_EVERY-th GEMM bracketed by events, as in the
-    # timed region), every schedule in turn, three rounds, so that clock and power drift falls on all of
+    # choose the schedule: blocks of K passes (each GEMM bracketed by events, as in the timed
+    # region), every schedule in turn, three rounds, so that clock and power drift falls on all of
     # them alike; the serial schedule (GEMM, consumer, post-reorder on one queue) is measured alike
     passes(scheds[0]["pipe"], a.warmup)
     order = [(i, False) for i in range(len(scheds))] + [(0, True)]
@@ -484,7 +519,7 @@ def main():
             passes(pipe, 5, serial=serial)
             t0 = time.perf_counter()
             for j in range(a.steps):
-                pipe.step(events={"gemm": pick_ev[j]} if j % EV_EVERY == 0 else None, serial=serial)
+                pipe.step(events={"gemm": pick_ev[j]}, serial=serial)
             pipe.join()
             torch.cuda.synchronize()
             picks[(i, serial)].append((time.perf_counter() - t0) * 1e3 / a.steps)
@@ -498,8 +533,8 @@ def main():
 
     # timed: five regions, each W warm-up passes then exactly K passes of the chosen schedule,
     # synchronised on both sides; a device event pair brackets each region (first GEMM's start to
-    # the last post-reorder's end) beside the host clock; the GEMM of every EV_EVERY-th pass is
-    # bracketed by events on its own stream for the roofline.  The value is the median region.  Before the
+    # the last post-reorder's end) beside the host clock; the GEMM of every pass is bracketed by
+    # events on its own stream for the roofline.  The value is the median region.  Before the
     # first region the chosen schedule runs 100 untimed passes, so no region starts in a clock ramp.
     passes(pipe, 100)
     reg = []
@@ -509,14 +544,14 @@ def main():
         t0 = time.perf_counter()
         region_ev[r][0].record(pipe.next_gemm_stream())
         for i in range(a.steps):
-            pipe.step(events={"gemm": gemm_ev[r][i]} if i % EV_EVERY == 0 else None)
+            pipe.step(events={"gemm": gemm_ev[r][i]})
         region_ev[r][1].record(pipe.post_stream)
         pipe.join()
         torch.cuda.synchronize()
         host_ms = (time.perf_counter() - t0) * 1e3 / a.steps
         launches[0] += a.steps
         check(pipe)
-        each = [s.elapsed_time(e) for i, (s, e) in enumerate(gemm_ev[r]) if i % EV_EVERY == 0]
+        each = [s.elapsed_time(e) for s, e in gemm_ev[r]]
         dev_ms = region_ev[r][0].elapsed_time(region_ev[r][1]) / a.steps
         reg.append(dict(host_ms=host_ms, device_ms=dev_ms, gemm_ms=float(np.mean(each)),
                         gemm_q=np.percentile(each, [10, 50, 90]).tolist(), launches=[first, launches[0]]))
@@ -617,7 +652,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": committed_traffic(w.name),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes": 2 * (w.M * w.K + w.N * w.K + w.M * w.N),
-                     "kernel": "signaling GEMM inside the timed passes (events on its own stream, every %d-th pass)" % EV_EVERY},
+                     "kernel": "signaling GEMM inside the timed passes (events on its own stream)"},
         "timed_regions": [{"host_ms_per_step": round(r["host_ms"], 4), "device_ms_per_step": round(r["device_ms"], 4),
                            "signal_gemm_ms": round(r["gemm_ms"], 4)} for r in reg],
         "timed_region_used": mid,
@@ -661,6 +696,7 @@ def main():
         p_.close()
     del scheds, pipe, plan
     torch.cuda.synchronize()
+    _HipEvent.destroy_all()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, peer, m_per, row_dest, best["comp"])
     print(json.dumps(line), flush=True)
