@@ -15,7 +15,9 @@
 // held at the first sample's latency below it and extended at the last
 // sample's bandwidth beyond it; a group's size is its span in bytes;
 // candidates are visited in cut-mask order (bit i set: a group ends after
-// wave i+1) and ties keep the first.
+// wave i+1); among equal predictions the one with more groups wins (it
+// starts communicating sooner and spreads the communication over more of
+// the computation, which the model does not price), then the first.
 //
 // Cost: 2^(T-1) candidates of O(T) each; T <= 24 keeps a search well under a
 // second on one core.  The waves come from the plan; its own composition is
@@ -78,6 +80,7 @@ extern "C" int fo_plan_search(const fo_plan *p, double gemm_seconds, const doubl
   const uint32_t candidates = 1u << (T - 1);
   double best = 0.0;
   uint32_t best_mask = 0;
+  int best_groups = 0;
   for (uint32_t mask = 0; mask < candidates; ++mask) {
     // comm_end(i) = max(compute_end(i), comm_end(i-1)) + latency(bytes of group i), comm_end(-1) = 0
     double comm_end = 0.0, bytes = 0.0;
@@ -92,9 +95,11 @@ extern "C" int fo_plan_search(const fo_plan *p, double gemm_seconds, const doubl
       }
     }
     if (all_seconds) all_seconds[mask] = comm_end;
-    if (mask == 0 || comm_end < best) {
+    const int groups = 1 + __builtin_popcount(mask);
+    if (mask == 0 || comm_end < best || (comm_end == best && groups > best_groups)) {
       best = comm_end;
       best_mask = mask;
+      best_groups = groups;
     }
   }
   int P = 0, run = 0;

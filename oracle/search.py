@@ -28,7 +28,11 @@ Readings:
 * a group's data size is its contiguous span in bytes (the sum of its
   tiles' elements times the element size);
 * candidates are walked in the order of ``enumerate_compositions`` (cut
-  masks 0 .. 2^(T-1)-1); among equal predictions the first one wins.
+  masks 0 .. 2^(T-1)-1); among equal predictions the one with more groups
+  wins (the page's listing keeps a strict minimum over a candidate order it
+  leaves open; more groups start communicating sooner and spread it over
+  more of the computation, which the model does not price), and among
+  those the first one.
 """
 
 from __future__ import annotations
@@ -102,7 +106,7 @@ def search(wave_bytes: Sequence[float], duration: float, curve_bytes: Sequence[f
     for comp in enumerate_compositions(T):
         t = predict(comp, wave_bytes, duration, curve_bytes, curve_seconds)
         all_t.append(t)
-        if best_t is None or t < best_t:
+        if best_t is None or t < best_t or (t == best_t and len(comp) > len(best)):
             best, best_t = comp, t
     return best, best_t, all_t
 

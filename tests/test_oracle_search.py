@@ -50,7 +50,18 @@ def test_free_communication_gives_the_gemm_duration_for_every_candidate():
     wb = [3.0, 5.0, 7.0, 2.0, 1.0]
     best, best_t, all_t = search(wb, 10.0, [1.0, 2.0], [0.0, 0.0])
     assert all(t == pytest.approx(10.0) for t in all_t)
-    assert best == (5,)                                   # ties: the first candidate (mask 0)
+    assert best == (1, 1, 1, 1, 1)                        # ties: the candidate with most groups
+
+
+def test_equal_predictions_go_to_the_partition_with_most_groups():
+    """A flat per-call cost shorter than a wave (worked by hand): every group's call ends a quarter wave
+    after its computation, before the next group's computation does, so every partition ends at
+    4 + 0.25; the tie goes to the partition with the most groups."""
+    wb = [1.0, 1.0, 1.0, 1.0]
+    cb, cs = [1.0, 100.0], [0.25, 0.25]
+    best, best_t, all_t = search(wb, 4.0, cb, cs)
+    assert all_t == [4.25] * 8
+    assert best == (1, 1, 1, 1) and best_t == 4.25
 
 
 def test_no_computation_sums_the_calls():
