@@ -184,6 +184,27 @@ struct GemmParams {
   uint64_t timeout_ticks;  // serialized waves only: bound on one barrier wait
 };
 
+// Slot i of the plan's slot table.  The table is read-only while a kernel runs
+// and a slot's index is the same for the whole workgroup, so it is read
+// through the constant address space: scalar loads, counted apart from the
+// vector memory operations, so fetching the next tile's descriptor does not
+// wait for the previous tile's stores to complete (a vector load would: the
+// wait for it counts them too).
+__device__ __forceinline__ TileDesc load_slot(const TileDesc *slots, int i) {
+  typedef const __attribute__((address_space(4))) TileDesc ConstTileDesc;
+  const ConstTileDesc &s = ((const ConstTileDesc *)slots)[i];
+  TileDesc t;
+  t.row0 = s.row0;
+  t.col0 = s.col0;
+  t.rows = s.rows;
+  t.cols = s.cols;
+  t.problem = s.problem;
+  t.group = s.group;
+  t.base = s.base;
+  t.band_stride = s.band_stride;
+  return t;
+}
+
 // Device-wide barrier number k of a cooperative launch: every workgroup arrives
 // once per barrier, so the k-th completes when the arrival count reaches
 // (k + 1) * gridDim.x.  The wait is bounded by the device wall clock: past the
@@ -332,18 +353,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
 
   // The tile a workgroup works on and its buffer resources.  A tile's first
   // NS-1 K-slices are issued as soon as the previous tile's staging area is
-  // free, before that tile's signal, so the signal's waits overlap them.  The
-  // slot table is read-only while the kernel runs and a slot's index is the
-  // same for the whole workgroup, so it is read through the constant address
-  // space: scalar loads, counted apart from the vector memory operations, so
-  // fetching the next tile's descriptor does not wait for this tile's stores
-  // to complete (a vector load would: the wait for it counts them too).
-  typedef const __attribute__((address_space(4))) TileDesc ConstTileDesc;
-  const ConstTileDesc *const slots = (const ConstTileDesc *)p.slots;
-  TileDesc t = slots[0];
+  // free, before that tile's signal, so the signal's waits overlap them.
+  TileDesc t = load_slot(p.slots, 0);
   __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, 0), rb = make_rsrc(p.B, 0);
   auto load_tile = [&](int bb) {
-    t = slots[bb];
+    t = load_slot(p.slots, bb);
     ra = make_rsrc(p.A + (int64_t)t.row0 * p.K, t.rows * row_bytes);
     rb = make_rsrc(p.B + (int64_t)t.problem * p.b_stride + (int64_t)t.col0 * p.K, t.cols * row_bytes);
   };
