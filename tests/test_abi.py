@@ -18,6 +18,21 @@ def _declared():
     return sorted(set(re.findall(r"\b(fo_[a-z_]+)\s*\(", src)))
 
 
+def test_library_is_built_from_the_current_sources():
+    """The library the tests load is at least as new as every source and header it is built from: a
+    build that failed leaves the previous library in place, and every other test would then check
+    that one instead."""
+    if os.environ.get("FO_LIB"):
+        pytest.skip("FO_LIB names another library")
+    lib_t = os.path.getmtime(fo.LIB_PATH)
+    pkg = os.path.join(ROOT, "gemm_tile_signaling_amd")
+    srcs = [os.path.join(ROOT, "include", "fo.h"), os.path.join(pkg, "build.py")]
+    for d, _, files in os.walk(os.path.join(pkg, "csrc")):
+        srcs += [os.path.join(d, f) for f in files if f.endswith((".cpp", ".hip", ".h"))]
+    stale = [os.path.relpath(f, ROOT) for f in srcs if os.path.getmtime(f) > lib_t]
+    assert not stale, f"libfo.so is older than {stale}: rebuild (python -m gemm_tile_signaling_amd.build)"
+
+
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"fo_plan_groups", "fo_gemm_signal", "fo_consume_group", "fo_reorder_post"} <= set(names)
