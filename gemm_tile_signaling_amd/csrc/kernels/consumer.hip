@@ -18,8 +18,9 @@
 // buckets); the stand-in's reduction is the same on each, so it streams the
 // span in one pass rather than paying a pass per unit.  The span is read
 // with device-coherent loads (the cache policy that agent-scope atomic loads
-// use), so data the producer released to device scope is read from the point
-// of coherence and no workgroup has to invalidate its L2 (a full-L2
+// use), so data the producer published at device scope (written through its
+// L2 and complete before the tile was counted) is read from the point of
+// coherence and no workgroup has to invalidate its L2 (a full-L2
 // invalidation per workgroup per group would evict the GEMM's operands and,
 // with many workgroups, dominate the kernel).  Every access is nontemporal:
 // each byte is touched once, and streaming it past the caches roughly doubles

@@ -55,7 +55,7 @@
 //     destination offset (row-major, banded or subtoken layout) is computed
 //     once into LDS; then 16-byte coalesced buffer stores, written through
 //     the L2 (system-scope cache policy).  Once every wave has read
-//     the staging tile, the workgroup issues the next tile's first two
+//     the staging tile, the workgroup issues the next tile's first NS-1
 //     K-slices.  With signaling on, each wave then waits for all its memory
 //     operations to complete (the tile's stores were written through the L2,
 //     so complete means visible to device-coherent loads), the workgroup
