@@ -192,6 +192,46 @@ def test_consumer_times_out_on_unsignalled_group_and_leaves_it_untouched():
     assert np.all(got[spans[2]:] == 0x7FC0)
 
 
+@pytest.mark.parametrize("tile,M,N", [((64, 64), 1024, 2048), ((128, 128), 2048, 4096), ((256, 128), 2048, 8192)])
+def test_polling_consumer_launched_first_stays_beside_the_gemm(tile, M, N):
+    """Residency: the persistent consumer (one workgroup per CU) is launched before the GEMM on another
+    queue and polls until the GEMM signals; a full wave of GEMM workgroups (W = the CU count, two waves)
+    must still find room beside it on every CU, or the consumer times out (bounded at 0.5 s) before the
+    GEMM can signal.  Every tile the polling consumer serves is checked (the 256 x 256 tile takes the
+    whole register file and is documented not to be paired with it)."""
+    K = 512
+    BM, BN = tile
+    p = fo.Plan([M], N, K, "bf16", BM=BM, BN=BN)     # W = the CU count, one group per wave
+    if p.NT != 2 * p.W:
+        p.close()
+        pytest.skip(f"the shapes give two waves on 256 CUs; this device has W = {p.W}")
+    say(f"polling consumer first, tile {BM}x{BN}, W={p.W}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    A = (torch.randn(M * K, device="cuda", generator=g) * 0.1).to(torch.bfloat16).view(torch.int16)
+    B = (torch.randn(N * K, device="cuda", generator=g) * 0.1).to(torch.bfloat16).view(torch.int16)
+    peer = torch.zeros(M * N, dtype=torch.int16, device="cuda")
+    buf = torch.empty(M * N, dtype=torch.int16, device="cuda")
+    recv = torch.empty_like(buf)
+    sig = p.new_sig()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sa, sb = fo.stream_create(), fo.stream_create()
+    torch.cuda.synchronize()
+    try:
+        for e in (1, 2):
+            recv.fill_(-1)
+            p.consume_group(buf, peer, recv, sig, e, status, timeout_us=500000, stream=sb)
+            p.gemm_signal(A, B, buf, sig, e, stream=sa)
+            torch.cuda.synchronize()
+            assert int(status.item()) == 0, fo.status_string(int(status.item()))
+            # peer is zero: every element of recv is its element of the GEMM's reordered output
+            assert torch.equal(recv, buf)
+    finally:
+        fo.stream_destroy(sa)
+        fo.stream_destroy(sb)
+        p.close()
+
+
 def test_consumer_group_range():
     entry = PLANS[1]
     o, p = _plans(entry)
