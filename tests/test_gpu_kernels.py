@@ -37,6 +37,7 @@ PLANS = [
     ("subtoken_d4", [70, 0, 130, 64], 192, 128, "bf16", 128, 128, 2, 3, None, "subtoken", 4),
     ("subtoken_d8_256", [300, 257, 1], 256, 64, "bf16", 256, 128, 1, 2, None, "subtoken", 8),
     ("fp16_256x128", [300, 200], 256, 192, "fp16", 256, 128, 1, 3, (1, 1), "tile", 1),
+    ("ragged_rows_cols_256x128", [300], 200, 128, "bf16", 256, 128, 2, 2, None, "tile", 1),
     # 256 x 256 tiles (K-slices of 32): ragged rows and columns, rank bands, fp16
     ("ragged_256x256", [600], 640, 192, "bf16", 256, 256, 2, 3, None, "tile", 1),
     ("subtile_r8_256x256", [512], 512, 128, "bf16", 256, 256, 1, 2, None, "subtile", 8),
