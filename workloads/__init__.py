@@ -56,8 +56,11 @@ WORKLOADS = {
                          compositions=((2,), (1, 1))),
     # tensor-parallel all-reduce share: Llama3-70B down projection, TP=8
     "ar_prefill": Workload("ar_prefill", 4096, 8192, 3584, "bf16", ("normal", 0.02), 30),
+    # S = 2: the two tile rows of a B column are neighbours in dispatch order and so share an XCD,
+    # whose L2 then reads that column of B once (with S = 1 they would sit on different XCDs: twice
+    # the HBM traffic, 8-10% slower)
     "ar_decode": Workload("ar_decode", 128, 8192, 3584, "bf16", ("normal", 0.02), 34,
-                          BM=64, BN=64, S=1),
+                          BM=64, BN=64, S=2),
     # reduce-scatter layout: Llama2-7B TP=4, R = 4 rank segments
     "rs": Workload("rs", 8192, 4096, 2752, "bf16", ("normal", 0.02), 40, mode="subtile", ranks=4),
     # MoE all-to-all: 8 experts, 4096 tokens, top-2, D = 8 destinations
