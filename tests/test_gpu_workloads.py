@@ -34,11 +34,12 @@ from gemm_tile_signaling_amd.pipeline import Pipeline  # noqa: E402
 CASES = [
     ("profiled", (2,), False, "poll"), ("profiled", (1, 1), False, "gated"), ("profiled", (1, 1), True, "gated"),
     ("profiled", (1, 1), True, "poll"),
-    ("ar_prefill", (1, 1, 1, 1), True, "gated"), ("ar_prefill", (2, 2), False, "poll"),
-    ("ar_prefill", (1, 3), False, "gated"),
-    ("ar_decode", (1,), False, "gated"),
-    ("rs", (1, 1, 1, 1), False, "poll"), ("rs", (1, 2, 1), True, "gated"),
+    ("ar_prefill", (1, 1, 1, 1), True, "gated"), ("ar_prefill", (1, 1, 1, 1), True, "poll"),
+    ("ar_prefill", (2, 2), False, "poll"), ("ar_prefill", (1, 3), False, "gated"),
+    ("ar_decode", (1,), False, "gated"), ("ar_decode", (1,), False, "poll"),
+    ("rs", (1, 1, 1, 1), False, "poll"), ("rs", (1, 1, 1, 1), True, "poll"), ("rs", (1, 2, 1), True, "gated"),
     ("moe_a2a", (4, 4, 4, 5), True, "gated"), ("moe_a2a", (1,) * 17, False, "poll"),
+    ("moe_a2a", (1,) * 17, True, "poll"),
 ]
 
 _cache = {}
