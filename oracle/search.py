@@ -42,7 +42,7 @@ from typing import List, Sequence, Tuple
 from .tiles import enumerate_compositions
 
 
-def interp_latency(curve_bytes: Sequence[float], curve_seconds: Sequence[float], size: float) -> float:
+def curve_latency(curve_bytes: Sequence[float], curve_seconds: Sequence[float], size: float) -> float:
     """Latency of one collective call on ``size`` bytes, from the sampled curve."""
     if len(curve_bytes) != len(curve_seconds) or len(curve_bytes) == 0:
         raise ValueError("curve needs matching, non-empty samples")
@@ -94,7 +94,7 @@ def predict(composition: Sequence[int], wave_bytes: Sequence[float], duration: f
     for waves, size in zip(composition, sizes):
         waves_done += waves
         compute_end = per_wave * waves_done
-        comm_end = max(compute_end, comm_end) + interp_latency(curve_bytes, curve_seconds, size)
+        comm_end = max(compute_end, comm_end) + curve_latency(curve_bytes, curve_seconds, size)
     return comm_end
 
 

@@ -11,7 +11,7 @@ import os
 import pytest
 
 import oracle
-from oracle.search import group_bytes, interp_latency, predict, search, wave_bytes_of
+from oracle.search import group_bytes, curve_latency, predict, search, wave_bytes_of
 from oracle.tiles import make_plan
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "search_toy.json")
@@ -36,14 +36,14 @@ def test_hand_evaluated_toy():
 def test_interpolation_at_samples_midpoints_and_ends():
     cb, cs = [10.0, 20.0, 40.0], [1.0, 3.0, 4.0]
     for b, s in zip(cb, cs):
-        assert interp_latency(cb, cs, b) == s
-    assert interp_latency(cb, cs, 15.0) == pytest.approx(2.0)
-    assert interp_latency(cb, cs, 30.0) == pytest.approx(3.5)
-    assert interp_latency(cb, cs, 5.0) == 1.0             # below the first sample: its latency
-    assert interp_latency(cb, cs, 80.0) == pytest.approx(8.0)   # beyond: the last sample's bandwidth
-    assert interp_latency(cb, cs, 0.0) == 0.0
+        assert curve_latency(cb, cs, b) == s
+    assert curve_latency(cb, cs, 15.0) == pytest.approx(2.0)
+    assert curve_latency(cb, cs, 30.0) == pytest.approx(3.5)
+    assert curve_latency(cb, cs, 5.0) == 1.0             # below the first sample: its latency
+    assert curve_latency(cb, cs, 80.0) == pytest.approx(8.0)   # beyond: the last sample's bandwidth
+    assert curve_latency(cb, cs, 0.0) == 0.0
     with pytest.raises(ValueError):
-        interp_latency([2.0, 2.0], [1.0, 1.0], 1.0)
+        curve_latency([2.0, 2.0], [1.0, 1.0], 1.0)
 
 
 def test_free_communication_gives_the_gemm_duration_for_every_candidate():
@@ -69,7 +69,7 @@ def test_no_computation_sums_the_calls():
     wb = [4.0, 1.0, 2.0, 8.0]
     cb, cs = [1.0, 16.0], [3.0, 6.0]                       # per-call cost 3 at 1 byte, +0.2 per byte
     for comp in oracle.enumerate_compositions(4):
-        want = sum(interp_latency(cb, cs, s) for s in group_bytes(comp, wb))
+        want = sum(curve_latency(cb, cs, s) for s in group_bytes(comp, wb))
         assert predict(comp, wb, 0.0, cb, cs) == pytest.approx(want)
     best, _, _ = search(wb, 0.0, cb, cs)
     assert best == (4,)                                   # a fixed per-call cost favours one call
