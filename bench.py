@@ -145,6 +145,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
     out = []
     s = streams[0]
     td = {"bf16": torch.bfloat16, "fp16": torch.float16}
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     # the prefill, ReduceScatter and MoE shapes keep two or more waves with 256 x 256 tiles as well
     runs = [("ar_prefill", None), ("ar_prefill", (256, 256)), ("ar_decode", None), ("rs", None), ("rs", (256, 256)),
             ("moe_a2a", None), ("moe_a2a", (256, 256))]
@@ -177,6 +178,15 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
         for _ in range(3):
             _sig(s)
         sig_ms, plain_ms = _time_pair(torch, _sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, 10)
+        # the matrix pipe's ceiling on this workload's A values (fo_mfma_rate), after the clock settles
+        pr_out = torch.empty(n_cu * 256, dtype=torch.float32, device=dev)
+
+        def _rate(st):
+            fo.mfma_rate(dA, pr_out, n_cu, 1280, dtype=w.dtype, stream=st)
+        for _ in range(200):
+            _rate(s)
+        rate_tflops = fo.mfma_rate_flops(n_cu, 1280) / (_time_kernel(torch, _rate, s, 20) * 1e-3) / 1e12
+        del pr_out
         # the schedule: gated or polling consumer, post-reorder per group or whole, chosen from
         # interleaved blocks of passes as for the headline; the polling consumer needs room beside the
         # GEMM's workgroups, which the 256 x 256 tile (every register of the SIMD) does not leave
@@ -227,6 +237,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
                "signal_gemm_in_pass_tflops": round(flops / (gemm_pipe_ms * 1e-3) / 1e12, 1),
                "signal_in_pass_over_plain": round(plain_ms / gemm_pipe_ms, 4),
                "frac_of_peak": round(flops / (gemm_pipe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "mfma_rate_workload_operands_tflops": round(rate_tflops, 1),
                "pass_ms": round(pass_ms, 4),
                "pass_tflops": round(flops / (pass_ms * 1e-3) / 1e12, 1),
                "schedules_ms": {f"{r['consumer']}, {'per group' if r['per_group'] else 'whole'}":
@@ -664,6 +675,23 @@ def main():
     torch.cuda.synchronize()
     lib_ms = _time_kernel(torch, _lib, s, n_alone)
     del c_mat
+    # the matrix pipe's ceiling on this data (fo_mfma_rate: MFMAs only, no loads, LDS or epilogue), one
+    # workgroup of four waves per CU, on operand values read from A (the GEMM's own distribution) and on
+    # zeros (no multiplier toggles); each after 200 untimed launches of about the GEMM's length, so the
+    # clock has settled under that load
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    pr_iters = 1280
+    pr_out = torch.empty(n_cu * 256, dtype=torch.float32, device=dev)
+    pr_zero = torch.zeros(4096, dtype=torch.int16, device=dev)
+    mfma_rate = {}
+    for key, ops in (("workload_operands_tflops", dA), ("zero_operands_tflops", pr_zero)):
+        def _rate(st, ops=ops):
+            fo.mfma_rate(ops, pr_out, n_cu, pr_iters, dtype=w.dtype, stream=st)
+        for _ in range(200):
+            _rate(s)
+        mfma_rate[key] = round(fo.mfma_rate_flops(n_cu, pr_iters) / (_time_kernel(torch, _rate, s, n_alone) * 1e-3)
+                               / 1e12, 1)
+    del pr_out, pr_zero
     mn = w.M * w.N
     consume_gbps = 6.0 * mn / (consume_ms * 1e-3) / 1e9
     gated_gbps = 6.0 * mn / (gated_ms * 1e-3) / 1e9
@@ -702,6 +730,9 @@ def main():
         "signal_over_plain_alone": round(plain_ms / signal_ms, 4),
         "signal_with_consumer_over_plain": round(plain_ms / best["gemm_ms"], 4),
         "context_library_gemm_tflops": round(flops / (lib_ms * 1e-3) / 1e12, 2),
+        "mfma_rate_probe": dict(mfma_rate, operands=f"A of the workload ({w.dist[0]}), and zeros",
+                                signal_gemm_in_pass_over_workload_operands=round(
+                                    achieved / mfma_rate["workload_operands_tflops"], 4)),
         "consumer_alone_gbps": round(consume_gbps, 1),
         "consumer_gated_alone_gbps": round(gated_gbps, 1),
         "post_reorder_alone_gbps": round(post_gbps, 1),

@@ -24,7 +24,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["Plan", "FoError", "lib", "LIB_PATH", "status_string", "stream_create", "stream_destroy",
-           "arch_supported", "FO_OK", "FO_ERR_INVALID", "FO_ERR_UNSUPPORTED", "FO_ERR_HIP", "FO_ERR_NOMEM",
+           "arch_supported", "mfma_rate", "mfma_rate_flops", "FO_OK", "FO_ERR_INVALID", "FO_ERR_UNSUPPORTED", "FO_ERR_HIP", "FO_ERR_NOMEM",
            "FO_ERR_TIMEOUT", "FO_ERR_STALE"]
 
 # FO_LIB names another build of the same library (the sanitizer build of the CPU tests)
@@ -98,6 +98,7 @@ def lib() -> C.CDLL:
             "fo_reorder_post_groups": [vp, i32, i32, vp, vp, vp],
             "fo_reorder_pre": [vp, vp, vp, vp],
             "fo_reorder_post_ep": [vp, vp, vp, vp, i32, vp],
+            "fo_mfma_rate": [i32, vp, i64, i32, i32, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -170,6 +171,22 @@ def stream_create():
 
 def stream_destroy(s):
     _check(lib().fo_stream_destroy(int(s.cuda_stream)), "fo_stream_destroy")
+
+
+def mfma_rate(ops, out, workgroups: int, iters: int, dtype: str = "bf16", stream=None):
+    """``fo_mfma_rate``: MFMAs only, on operand values read from ``ops`` (a measurement aid for the GEMM's
+    roofline).  ``out``: float32 device tensor of ``workgroups * 256`` elements."""
+    nbytes = ops.numel() * ops.element_size() if hasattr(ops, "numel") else None
+    if nbytes is None:
+        raise TypeError("ops: expected a device tensor")
+    _check(lib().fo_mfma_rate(_DTYPES[dtype], _ptr(ops, name="ops"), nbytes, int(workgroups), int(iters),
+                              _ptr(out, numel=int(workgroups) * 256, itemsize=4, name="out"), _stream(stream)),
+           "fo_mfma_rate")
+
+
+def mfma_rate_flops(workgroups: int, iters: int) -> float:
+    """FLOP of one ``mfma_rate`` launch: 4 waves x ``iters`` rounds x 8 MFMAs of 32x32x16 per workgroup."""
+    return float(workgroups) * 4 * iters * 8 * 2 * 32 * 32 * 16
 
 
 class Plan:

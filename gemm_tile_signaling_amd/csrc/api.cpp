@@ -154,6 +154,15 @@ int fo_reorder_pre(const fo_plan *p, const void *in, void *reordered, hipStream_
   return fo::launch_reorder(p, in, reordered, false, 0, p->NT, stream);
 }
 
+int fo_mfma_rate(int32_t dtype, const void *ops, int64_t ops_bytes, int32_t workgroups, int32_t iters, float *out,
+                 hipStream_t stream) {
+  if (dtype != FO_BF16 && dtype != FO_FP16) return FO_ERR_INVALID;
+  if (!ops || !aligned16(ops) || ops_bytes < 16 || ops_bytes % 16 != 0) return FO_ERR_INVALID;
+  if (workgroups < 1 || workgroups > 65536 || iters < 0) return FO_ERR_INVALID;
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 3u)) return FO_ERR_INVALID;
+  return fo::launch_mfma_rate(dtype, ops, ops_bytes, workgroups, iters, out, stream);
+}
+
 int fo_stream_create(hipStream_t *out) {
   if (!out) return FO_ERR_INVALID;
   int dev = 0, cus = 0;

@@ -140,5 +140,7 @@ int launch_row_exchange(const fo_plan *p, const void *gathered, void *out, const
 int launch_reorder(const fo_plan *p, const void *src, void *dst, bool to_rowmajor, int32_t slot_begin,
                    int32_t slot_end, hipStream_t s);
 int launch_post_ep(const fo_plan *p, const void *src, void *dst, const void *bias, int act, hipStream_t s);
+int launch_mfma_rate(int dtype, const void *ops, int64_t ops_bytes, int32_t workgroups, int32_t iters, float *out,
+                     hipStream_t s);
 
 }  // namespace fo

@@ -472,6 +472,26 @@ int fo_row_exchange(const fo_plan *plan, const void *gathered, void *out, const 
 int fo_stream_create(hipStream_t *out);
 int fo_stream_destroy(hipStream_t stream);
 
+/*
+ * Measurement aid for the signaling GEMM's roofline, not a step of the method
+ * (the pages time their GEMM against its hardware; deep-dive 三 › 调优挑战).
+ * Runs nothing but v_mfma_f32_32x32x16 (dtype: fo_dtype, bf16 or fp16) on
+ * operand registers read from `ops`, so its rate is the matrix pipe's ceiling
+ * for those values at the clock the part keeps under the load -- without the
+ * GEMM's loads, LDS traffic or epilogue.  `workgroups` workgroups of 256
+ * threads (four waves, one per SIMD); every lane reads 16 vectors of 16 bytes
+ * from `ops` (lane i's vectors 16i .. 16i+15, indices modulo ops_bytes / 16:
+ * the first 8 are A operands, the next 8 B operands), then runs `iters` rounds
+ * of 8 independent MFMAs, one per (A, B) pair, and stores the sum of its
+ * accumulators in out[lane] (fp32, summed in register order).
+ *   FLOP per launch = workgroups * 4 * iters * 8 * 2 * 32 * 32 * 16.
+ * ops: device, 16-byte aligned, ops_bytes a positive multiple of 16; out:
+ * device float[workgroups * 256]; 1 <= workgroups <= 65536; 0 <= iters.
+ * FO_ERR_INVALID on any other argument; FO_ERR_HIP if the launch fails.
+ */
+int fo_mfma_rate(int32_t dtype, const void *ops, int64_t ops_bytes, int32_t workgroups, int32_t iters, float *out,
+                 hipStream_t stream);
+
 /* Static description of a status code. */
 const char *fo_status_string(int code);
 

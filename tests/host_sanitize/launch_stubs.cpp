@@ -27,6 +27,7 @@ int launch_reorder(const fo_plan *, const void *, void *, bool, int32_t, int32_t
   return FO_ERR_UNSUPPORTED;
 }
 int launch_post_ep(const fo_plan *, const void *, void *, const void *, int, hipStream_t) { return FO_ERR_UNSUPPORTED; }
+int launch_mfma_rate(int, const void *, int64_t, int32_t, int32_t, float *, hipStream_t) { return FO_ERR_UNSUPPORTED; }
 
 }  // namespace fo
 

@@ -161,3 +161,18 @@ def test_new_enqueue_calls_reject_host_only_and_wrong_layouts():
     assert _code(lambda: p.consume_group_gated(16, 16, 16, 16, 1, 16, trace=20, stream=0)) == -1
     assert _code(lambda: p.reorder_shards(16, 16, stream=0)) == -1
     assert _code(lambda: p.row_exchange(16, 16, stream=0)) == -1
+
+
+def test_mfma_rate_argument_errors():
+    L = fo.lib()
+    out = 256                       # a 4-aligned address; nothing is launched on a refused call
+    assert L.fo_mfma_rate(2, 16, 16, 1, 1, out, None) == -1          # dtype
+    assert L.fo_mfma_rate(0, 0, 16, 1, 1, out, None) == -1           # no operands
+    assert L.fo_mfma_rate(0, 8, 16, 1, 1, out, None) == -1           # misaligned operands
+    assert L.fo_mfma_rate(0, 16, 0, 1, 1, out, None) == -1           # empty
+    assert L.fo_mfma_rate(0, 16, 24, 1, 1, out, None) == -1          # not whole vectors
+    assert L.fo_mfma_rate(0, 16, 16, 0, 1, out, None) == -1          # no workgroups
+    assert L.fo_mfma_rate(0, 16, 16, 65537, 1, out, None) == -1      # too many
+    assert L.fo_mfma_rate(0, 16, 16, 1, -1, out, None) == -1         # negative rounds
+    assert L.fo_mfma_rate(0, 16, 16, 1, 1, 0, None) == -1            # no output
+    assert L.fo_mfma_rate(0, 16, 16, 1, 1, 258, None) == -1          # misaligned output
