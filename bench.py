@@ -168,6 +168,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
         plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=BM, BN=BN, swizzle=w.S, wave_size=w.W, composition=comp,
                        mode=w.mode, ranks=w.ranks, row_dest=row_dest)
         flops = 2.0 * M * w.N * w.K
+        alg_bytes = 2.0 * (M * w.K + len(m_per) * w.N * w.K + M * w.N)
         C = torch.empty(M * w.N, dtype=torch.int16, device=dev)
         sig = plan.new_sig(dev)
         ep = [0]
@@ -238,6 +239,12 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
                "signal_in_pass_over_plain": round(plain_ms / gemm_pipe_ms, 4),
                "frac_of_peak": round(flops / (gemm_pipe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                "mfma_rate_workload_operands_tflops": round(rate_tflops, 1),
+               # which roof bounds this shape: its arithmetic intensity (FLOP per algorithmic HBM byte:
+               # A, every problem's B and C once each) against the ridge of the two peaks
+               "flop_per_byte": round(flops / alg_bytes, 1),
+               "bound": "mfma" if flops / alg_bytes >= PEAK_BF16_TFLOPS / PEAK_HBM_GBPS * 1e3 else "hbm",
+               "gemm_in_pass_hbm_gbps": round(alg_bytes / (gemm_pipe_ms * 1e-3) / 1e9, 1),
+               "gemm_in_pass_frac_hbm": round(alg_bytes / (gemm_pipe_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                "pass_ms": round(pass_ms, 4),
                "pass_tflops": round(flops / (pass_ms * 1e-3) / 1e12, 1),
                "schedules_ms": {f"{r['consumer']}, {'per group' if r['per_group'] else 'whole'}":
