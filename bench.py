@@ -450,12 +450,25 @@ def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, min_seconds=10.0):
 
     v, threads, reps, dt = run(w.M, nproc, min_seconds, 50)
     v1, _, reps1, dt1 = run(min(512, w.M), 1, 0.0, 1)
+    # one more threaded pass, stage by stage (seconds), as the oracle times its own steps
+    stages = {}
+    with threadpool_limits(limits=nproc):
+        oracle.run_pipeline(A, B, peer, make_plan([w.M], w.N, BM=w.BM, BN=w.BN, S=w.S, W=w.W, composition=comp,
+                                                  mode=w.mode, ranks=w.ranks, row_dest=row_dest),
+                            w.dtype, stage_seconds=stages)
+    mn = w.M * w.N
+    stage_rates = {"gemm_tflops": 2.0 * w.M * w.N * w.K / stages["gemm"] / 1e12,
+                   "consume_gbps": 6.0 * mn / stages["consume"] / 1e9,
+                   "pre_reorder_gbps": 4.0 * mn / stages["pre_reorder"] / 1e9,
+                   "post_reorder_gbps": 4.0 * mn / stages["post_reorder"] / 1e9}
     return dict(value=round(v, 4), unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample=f"full workload (M={w.M}, N={w.N}, K={w.K}, groups {tuple(comp)}) x {reps} passes, "
                        f"{dt:.1f} s, BLAS pool {threads} threads",
                 single_thread=dict(value=round(v1, 4), unit="TFLOP/s",
                                    sample=f"first {min(512, w.M)} rows x 1 pass, {dt1:.1f} s, 1 thread"),
-                nproc=int(nproc), cpu_model=_cpu_model())
+                nproc=int(nproc), cpu_model=_cpu_model(),
+                stages_s={k: round(t, 4) for k, t in stages.items()},
+                stage_rates={k: round(r, 3) for k, r in stage_rates.items()})
 
 
 def main():

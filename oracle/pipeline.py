@@ -18,7 +18,8 @@ identically reordered span).  All bit arrays are uint16 patterns of
 
 from __future__ import annotations
 
-from typing import Dict, List
+import time
+from typing import Dict, List, Optional
 
 import numpy as np
 
@@ -35,14 +36,25 @@ def _problem_rows(plan: Plan) -> List[int]:
     return starts
 
 
-def run_pipeline(A_bits, B_bits: List[np.ndarray], peer_bits, plan: Plan, dtype: str) -> Dict:
+def run_pipeline(A_bits, B_bits: List[np.ndarray], peer_bits, plan: Plan, dtype: str,
+                 stage_seconds: Optional[Dict[str, float]] = None) -> Dict:
     """Every intermediate of the path for one batch.
 
     Returns C64 (fp64 product), C (rounded bits, row-major), off (element
     offsets), send (pre-reordered C), recv (consumer result, flat), out
     (post-reordered recv, row-major), the counting-table trajectory and the
-    fire waves, the mapping tables and the consumer units.
+    fire waves, the mapping tables and the consumer units.  ``stage_seconds``,
+    if given, receives the wall time of each stage (gemm, offsets, pre_reorder,
+    consume, post_reorder, tables); it changes nothing else.
     """
+    clock = [time.perf_counter()]
+
+    def lap(name):
+        now = time.perf_counter()
+        if stage_seconds is not None:
+            stage_seconds[name] = stage_seconds.get(name, 0.0) + now - clock[0]
+        clock[0] = now
+
     A = decode_bits(A_bits, dtype)
     if len(B_bits) != len(plan.m_per_problem):
         raise ValueError("one B per problem")
@@ -52,17 +64,23 @@ def run_pipeline(A_bits, B_bits: List[np.ndarray], peer_bits, plan: Plan, dtype:
         Be = decode_bits(B_bits[e], dtype)          # stored [N, K]
         C64[r0:r0 + m] = gemm_fp64(A[r0:r0 + m], Be.T)
     C = encode_bits(round_to_dtype(C64, dtype), dtype)
+    lap("gemm")
     off = element_offsets(plan)
+    lap("offsets")
     send = pre_reorder(C, off)
+    lap("pre_reorder")
     recv = send.copy()
     units = consumer_units(plan)
     peer = np.asarray(peer_bits, dtype=np.uint16).ravel()
     for group in units:                       # groups in firing order
         for lo, hi in group:
             recv[lo:hi] = consume_add(send[lo:hi], peer[lo:hi], dtype)
+    lap("consume")
     out = post_reorder(recv, off)
+    lap("post_reorder")
     snaps, fire = counting_trajectory(plan)
     slot_of_tile, tile_of_slot = mapping_table(plan)
+    lap("tables")
     return dict(C64=C64, C=C, off=off, send=send, recv=recv, out=out,
                 snapshots=snaps, fire_wave=fire, slot_of_tile=slot_of_tile,
                 tile_of_slot=tile_of_slot, units=units)
