@@ -68,6 +68,7 @@ struct fo_plan {
   int32_t NT = 0, T = 0, P = 0;
   int32_t mode = 0, ranks = 1, dtype = 0, num_problems = 1;
   int32_t band_rows = 0;
+  int32_t min_tile_rows = 0, min_tile_cols = 0;  // smallest extent of any tile (ragged edges)
   uint32_t flags = 0;             // FO_PLAN_* bits
   bool host_only = false;
   bool can_wait_value = false;    // the device's queues can wait on a memory value

@@ -306,7 +306,10 @@ __device__ __forceinline__ void static_for(F &&f) {
 // physical and each wave's counting table can be read back; every workgroup
 // then runs exactly T iterations, idling through the tile work of a partial
 // last wave.
-template <typename T, int BM, int BN, int BK, int NW, bool SIGNAL, bool SERIAL>
+// SKIP (plans with ragged tiles only): a wave whose part of the tile lies
+// wholly past its edge skips its fragment reads and MFMAs; a separate
+// instantiation, so full-tile plans run code without the branch.
+template <typename T, int BM, int BN, int BK, int NW, bool SIGNAL, bool SERIAL, bool SKIP>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN, BK, NW>;
   constexpr int kRowBytes = C::ROWB;
@@ -451,61 +454,91 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
     constexpr int D = C::DIST, KS = C::KS, LAST = (KS - 1) % 2;
     wait_slices<C::LOADS, D - 1>(nk - 1);
     bare_barrier();
-    read_frags(0, 0, 0);
-    // The last slice is peeled off so that the loop body has no join point at
-    // which the wait-count insertion would have to assume the worst of two paths.
-    auto blocks_dma = [&](int kt) {  // blocks 0 .. KS-2, with parts 0 .. KS-2 of slice kt+D's loads
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<0, KS - 1>([&](auto sc) {
-        constexpr int st = decltype(sc)::value;
-        constexpr int left = C::LOADS - st * DPB;
-        FO_DMA_PART(st, kt + D);
-        read_frags((st + 1) % 2, kt, st + 1);
-        mfmas(st % 2);
-        block_order_dma(std::integral_constant<int, (left < 0 ? 0 : left < DPB ? left : DPB)>{});
-      });
-    };
-    auto blocks = [&](int kt) {
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<0, KS - 1>([&](auto sc) {
-        constexpr int st = decltype(sc)::value;
-        read_frags((st + 1) % 2, kt, st + 1);
-        mfmas(st % 2);
+    // With SKIP, a wave whose rows or columns of the tile lie wholly past its
+    // edge (an expert's last, mostly empty tile row) has nothing to multiply:
+    // it runs the second loop below, the same loads, waits and barriers in the
+    // same order (its loads fill LDS for the other waves) without fragment
+    // reads or MFMAs, so its SIMD's matrix pipe serves the other wave of the
+    // pair alone.  Without SKIP the condition is a constant and only the first
+    // loop exists.  wm, wn and the tile's extent are the same in every lane.
+    bool multiplies = true;
+    if constexpr (SKIP) multiplies = wm * C::WM < t.rows && wn * C::WN < t.cols;
+    if (multiplies) {
+      read_frags(0, 0, 0);
+      // The last slice is peeled off so that the loop body has no join point at
+      // which the wait-count insertion would have to assume the worst of two paths.
+      auto blocks_dma = [&](int kt) {  // blocks 0 .. KS-2, with parts 0 .. KS-2 of slice kt+D's loads
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, KS - 1>([&](auto sc) {
+          constexpr int st = decltype(sc)::value;
+          constexpr int left = C::LOADS - st * DPB;
+          FO_DMA_PART(st, kt + D);
+          read_frags((st + 1) % 2, kt, st + 1);
+          mfmas(st % 2);
+          block_order_dma(std::integral_constant<int, (left < 0 ? 0 : left < DPB ? left : DPB)>{});
+        });
+      };
+      auto blocks = [&](int kt) {
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, KS - 1>([&](auto sc) {
+          constexpr int st = decltype(sc)::value;
+          read_frags((st + 1) % 2, kt, st + 1);
+          mfmas(st % 2);
+          block_order();
+        });
+      };
+      // Steady state: one path per iteration, so the accumulators keep their
+      // registers from one iteration to the next.
+      int kt = 0;
+      for (; kt + D < nk; ++kt) {
+        blocks_dma(kt);
+        FO_DMA_PART(KS - 1, kt + D);
+        // this wave's reads of slice kt are complete and its loads of slice kt+1
+        // landed (slices kt+2 .. kt+D may still be in flight)
+        __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * C::LOADS));
+        bare_barrier();  // no wave reads slice kt any more; slice kt+1 is in LDS for every wave
+        read_frags(0, kt + 1, 0);
+        mfmas(LAST);
         block_order();
-      });
-    };
-    // Steady state: one path per iteration, so the accumulators keep their
-    // registers from one iteration to the next.
-    int kt = 0;
-    for (; kt + D < nk; ++kt) {
-      blocks_dma(kt);
-      FO_DMA_PART(KS - 1, kt + D);
-      // this wave's reads of slice kt are complete and its loads of slice kt+1
-      // landed (slices kt+2 .. kt+D may still be in flight)
-      __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * C::LOADS));
-      bare_barrier();  // no wave reads slice kt any more; slice kt+1 is in LDS for every wave
-      read_frags(0, kt + 1, 0);
+      }
+      // the last handovers: nothing left to load, slices kt+2 .. nk-1 in flight
+      auto drain = [&](int kt) {
+        blocks(kt);
+        __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+        wait_slices<C::LOADS, D - 2>(nk - 2 - kt);
+        bare_barrier();
+        read_frags(0, kt + 1, 0);
+        mfmas(LAST);
+        block_order();
+      };
+      if constexpr (D == 2) {
+        if (kt + 1 < nk) drain(kt++);
+      } else {
+        for (; kt + 1 < nk; ++kt) drain(kt);
+      }
+      blocks(nk - 1);
       mfmas(LAST);
-      block_order();
-    }
-    // the last handovers: nothing left to load, slices kt+2 .. nk-1 in flight
-    auto drain = [&](int kt) {
-      blocks(kt);
-      __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
-      wait_slices<C::LOADS, D - 2>(nk - 2 - kt);
-      bare_barrier();
-      read_frags(0, kt + 1, 0);
-      mfmas(LAST);
-      block_order();
-    };
-    if constexpr (D == 2) {
-      if (kt + 1 < nk) drain(kt++);
     } else {
-      for (; kt + 1 < nk; ++kt) drain(kt);
+      // the barrier skeleton of the loop above: slice kt+D's loads (all KS
+      // parts) during slice kt, then the same waits and one barrier per slice
+      int kt = 0;
+      for (; kt + D < nk; ++kt) {
+        static_for<0, KS>([&](auto part) { FO_DMA_PART(decltype(part)::value, kt + D); });
+        __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * C::LOADS));
+        bare_barrier();
+      }
+      auto drain_idle = [&](int kt) {
+        wait_slices<C::LOADS, D - 2>(nk - 2 - kt);
+        bare_barrier();
+      };
+      if constexpr (D == 2) {
+        if (kt + 1 < nk) drain_idle(kt++);
+      } else {
+        for (; kt + 1 < nk; ++kt) drain_idle(kt);
+      }
     }
-    blocks(nk - 1);
-    mfmas(LAST);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // all fragment reads done before the staging tile overwrites the ring
 
@@ -590,10 +623,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
 #undef FO_DMA_PART
 }
 
-template <typename T, int BM, int BN, int BK, int NW, bool SIGNAL, bool SERIAL>
+template <typename T, int BM, int BN, int BK, int NW, bool SIGNAL, bool SERIAL, bool SKIP = false>
 int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
   using C = Cfg<BM, BN, BK, NW>;
-  const void *fn = reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, NW, SIGNAL, SERIAL>);
+  const void *fn = reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, NW, SIGNAL, SERIAL, SKIP>);
   static bool configured = false;  // per process; the attribute is per kernel and device-independent
   if (!configured) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess) return FO_ERR_HIP;
@@ -611,7 +644,8 @@ int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
       return FO_ERR_HIP;
     return FO_OK;
   } else {
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, NW, SIGNAL, false>), dim3(gp.W), dim3(C::THREADS), C::LDS, s, gp);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, NW, SIGNAL, false, SKIP>), dim3(gp.W), dim3(C::THREADS), C::LDS, s,
+                       gp);
     return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
   }
 }
@@ -619,7 +653,17 @@ int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
 template <typename T, bool SIGNAL, bool SERIAL>
 int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
   if (p->BM == 256 && p->BN == 256) return launch_typed<T, 256, 256, 32, 4, SIGNAL, SERIAL>(p, gp, s);
-  if (p->BM == 256 && p->BN == 128) return launch_typed<T, 256, 128, 64, 8, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 256 && p->BN == 128) {
+    // two waves share each SIMD: on a tile with an empty 64-row or 64-column
+    // band, the band's waves skipping their MFMAs lets the other wave of each
+    // pair run alone (only the 8-wave layout gains from it)
+    using C8 = Cfg<256, 128, 64, 8>;
+    if constexpr (!SERIAL) {
+      if (p->min_tile_rows <= 256 - C8::WM || p->min_tile_cols <= 128 - C8::WN)
+        return launch_typed<T, 256, 128, 64, 8, SIGNAL, SERIAL, true>(p, gp, s);
+    }
+    return launch_typed<T, 256, 128, 64, 8, SIGNAL, SERIAL>(p, gp, s);
+  }
   if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, 64, 4, SIGNAL, SERIAL>(p, gp, s);
   if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, 64, 4, SIGNAL, SERIAL>(p, gp, s);
   return FO_ERR_UNSUPPORTED;

@@ -228,6 +228,12 @@ int build(const fo_plan_desc *d, fo_plan *p) {
     p->slots[s] = tiles[p->tile_of_slot[s]];
     p->slots[s].group = p->group_of_slot[s];
   }
+  p->min_tile_rows = p->BM;
+  p->min_tile_cols = p->BN;
+  for (const fo::TileDesc &t : p->slots) {
+    p->min_tile_rows = std::min(p->min_tile_rows, t.rows);
+    p->min_tile_cols = std::min(p->min_tile_cols, t.cols);
+  }
   p->span_off.assign(p->P + 1, 0);
   for (int32_t s = 0; s < p->NT; ++s)
     p->span_off[p->group_of_slot[s] + 1] += (int64_t)p->slots[s].rows * p->slots[s].cols;

@@ -38,6 +38,9 @@ PLANS = [
     ("subtoken_d8_256", [300, 257, 1], 256, 64, "bf16", 256, 128, 1, 2, None, "subtoken", 8),
     ("fp16_256x128", [300, 200], 256, 192, "fp16", 256, 128, 1, 3, (1, 1), "tile", 1),
     ("ragged_rows_cols_256x128", [300], 200, 128, "bf16", 256, 128, 2, 2, None, "tile", 1),
+    # 256 x 128 tiles whose 64-row or 64-column wave bands lie wholly past the edge (1, 3 and 1 of 4 row
+    # bands hold rows; the last column tile has one of its two column bands): those waves skip their MFMAs
+    ("empty_bands_256x128", [40, 130, 300], 320, 192, "bf16", 256, 128, 2, 5, None, "tile", 1),
     # 256 x 256 tiles (K-slices of 32): ragged rows and columns, rank bands, fp16
     ("ragged_256x256", [600], 640, 192, "bf16", 256, 256, 2, 3, None, "tile", 1),
     ("subtile_r8_256x256", [512], 512, 128, "bf16", 256, 256, 1, 2, None, "subtile", 8),
