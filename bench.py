@@ -419,6 +419,29 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def gpu_info():
+    """The board's clock limits, memory clock and power cap, read through amdsmi (read-only); None where it is
+    not available.  The clock the GEMM actually runs at comes from the counter passes in profiles/ (GPU-active
+    cycles over the kernel's duration): the sampled clock reading does not follow a load this short."""
+    try:
+        import amdsmi
+    except ImportError:
+        return None
+    try:
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            gfx = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            mem = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
+            cap = amdsmi.amdsmi_get_power_cap_info(h)
+            return dict(sclk_min_mhz=gfx.get("min_clk"), sclk_max_mhz=gfx.get("max_clk"), mclk_mhz=mem.get("clk"),
+                        power_cap_w=round(cap.get("power_cap", 0) / 1e6, 1) if cap.get("power_cap") else None)
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception as e:  # noqa: BLE001 -- a monitoring read must never stop the benchmark
+        return dict(error=f"{type(e).__name__}: {e}")
+
+
 def cpu_baseline(w, A, B, peer, m_per, row_dest, comp, min_seconds=10.0):
     """The oracle pipeline (fp64 GEMM, pre-reorder, consumer, post-reorder) on the host cores.
 
@@ -768,6 +791,7 @@ def main():
                        "gemm_ms": round(r["br_gemm_ms"], 4), "consume_span_ms": round(r["consume_ms"], 4),
                        "post_ms": round(r["post_ms"], 4)} for r in scheds],
         "timed_signal_gemm_launches": timed_range,
+        "gpu": gpu_info(),
         "cpu_baseline": None,
     }
     for r in scheds:
