@@ -705,6 +705,26 @@ def main():
                                                                         else torch.float16).view(torch.int16)
     post_ep_ms = _time_kernel(torch, lambda st: plan.reorder_post_ep(recv, C, bias=bias, act="silu", stream=st), s,
                               n_alone, scratch)
+    # context: torch's own device copy of the same bytes (read M*N, write M*N elements), MALL flushed alike
+    cp_src = torch.ones(w.M * w.N, dtype=torch.int16, device=dev)
+
+    def _copy(st):
+        with torch.cuda.stream(st):
+            C.copy_(cp_src)
+    for _ in range(3):   # first launches load the kernel's code
+        _copy(s)
+    copy_ms = _time_kernel(torch, _copy, s, n_alone, scratch)
+    # and torch's elementwise add of two such buffers into a third (the consumer's bytes)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    add_a, add_b, add_c = pipe.buf.view(tdt), dpeer.view(tdt), C.view(tdt)
+
+    def _add(st):
+        with torch.cuda.stream(st):
+            torch.add(add_a, add_b, out=add_c)
+    for _ in range(3):
+        _add(s)
+    add_ms = _time_kernel(torch, _add, s, n_alone, scratch)
+    del cp_src, add_a, add_b, add_c
     # context only: the library GEMM (hipBLASLt through torch) on the same operands, C = A . B^T
     a_mat = dA.view(torch.bfloat16 if w.dtype == "bf16" else torch.float16).view(w.M, w.K)
     b_mat = dB.view(a_mat.dtype).view(w.N, w.K)
@@ -779,6 +799,8 @@ def main():
         "consumer_alone_gbps": round(consume_gbps, 1),
         "consumer_gated_alone_gbps": round(gated_gbps, 1),
         "post_reorder_alone_gbps": round(post_gbps, 1),
+        "context_torch_copy_gbps": round(4.0 * w.M * w.N / (copy_ms * 1e-3) / 1e9, 1),
+        "context_torch_add_gbps": round(6.0 * w.M * w.N / (add_ms * 1e-3) / 1e9, 1),
         "post_reorder_bias_silu_alone_gbps": round((4.0 * mn + 2.0 * plan.num_problems * w.N) / (post_ep_ms * 1e-3)
                                                    / 1e9, 1),
         "consumer_frac_hbm": round(max(consume_gbps, gated_gbps) / PEAK_HBM_GBPS, 4),
