@@ -189,10 +189,9 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
         rate_tflops = fo.mfma_rate_flops(n_cu, 1280) / (_time_kernel(torch, _rate, s, 20) * 1e-3) / 1e12
         del pr_out
         # the schedule: gated or polling consumer, post-reorder per group or whole, chosen from
-        # interleaved blocks of passes as for the headline; the polling consumer needs room beside the
-        # GEMM's workgroups, which the 256 x 256 tile (every register of the SIMD) does not leave
+        # interleaved blocks of passes as for the headline
         scheds = []
-        for consumer in (("gated",) if (BM, BN) == (256, 256) else ("gated", "poll")):
+        for consumer in ("gated", "poll"):
             for per_group in ((True, False) if plan.P > 1 else (False,)):
                 scheds.append(dict(consumer=consumer, per_group=per_group, ms=[],
                                    pipe=Pipeline(plan, dA, dB, dpeer, streams=streams, consumer=consumer,

@@ -58,6 +58,10 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;            // 16-byte chunks in flight per thread (4 was 5% slower gated)
+// Beside a 256 x 256 GEMM workgroup (two 232-register waves per SIMD) a SIMD
+// has 48 registers left: two chunks in flight per thread keep the consumer
+// under that (43 registers against 89), so it can run beside the GEMM.
+constexpr int kUnrollSlim = 2;
 constexpr int kNT = 2;              // buffer cache policy: nontemporal (each byte is streamed once)
 constexpr int kCoherent = 16;       // buffer cache policy: device-coherent load
 
@@ -189,6 +193,26 @@ ConsumeParams params(const fo_plan *p, const void *send, const void *peer, void 
   return cp;
 }
 
+// The consumer's waves run beside the GEMM's on the same SIMDs: with a 256 x
+// 256 GEMM tile only the slim form fits.
+bool slim(const fo_plan *p) { return p->BM == 256 && p->BN == 256; }
+
+template <bool GATED>
+void launch_form(const fo_plan *p, const ConsumeParams &cp, int32_t grid, hipStream_t s) {
+  const bool bf = p->dtype == FO_BF16;
+  if (slim(p)) {
+    if (bf)
+      hipLaunchKernelGGL((consume_kernel<__bf16, kUnrollSlim, GATED>), dim3(grid), dim3(kThreads), 0, s, cp);
+    else
+      hipLaunchKernelGGL((consume_kernel<_Float16, kUnrollSlim, GATED>), dim3(grid), dim3(kThreads), 0, s, cp);
+  } else {
+    if (bf)
+      hipLaunchKernelGGL((consume_kernel<__bf16, kUnroll, GATED>), dim3(grid), dim3(kThreads), 0, s, cp);
+    else
+      hipLaunchKernelGGL((consume_kernel<_Float16, kUnroll, GATED>), dim3(grid), dim3(kThreads), 0, s, cp);
+  }
+}
+
 }  // namespace
 
 int launch_consume(const fo_plan *p, const void *send, const void *peer, void *recv, const uint32_t *sig,
@@ -196,10 +220,7 @@ int launch_consume(const fo_plan *p, const void *send, const void *peer, void *r
                    int32_t grid, uint64_t *trace, hipStream_t s) {
   if (g_begin >= g_end) return FO_OK;
   const ConsumeParams cp = params(p, send, peer, recv, sig, epoch, g_begin, g_end, status, timeout_ticks, trace);
-  if (p->dtype == FO_BF16)
-    hipLaunchKernelGGL((consume_kernel<__bf16, kUnroll, false>), dim3(grid), dim3(kThreads), 0, s, cp);
-  else
-    hipLaunchKernelGGL((consume_kernel<_Float16, kUnroll, false>), dim3(grid), dim3(kThreads), 0, s, cp);
+  launch_form<false>(p, cp, grid, s);
   return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
 }
 
@@ -209,12 +230,9 @@ int launch_consume_ready(const fo_plan *p, const void *send, const void *peer, v
   const ConsumeParams cp = params(p, send, peer, recv, sig, epoch, g, g + 1, status, 2000000ull * p->ticks_per_us,
                                   trace);
   const int64_t chunks = (p->unit_off[p->group_unit[g + 1]] - p->unit_off[p->group_unit[g]]) / 8;
-  const int64_t per_wg = (int64_t)kThreads * kUnroll;
+  const int64_t per_wg = (int64_t)kThreads * (slim(p) ? kUnrollSlim : kUnroll);
   const int32_t grid = (int32_t)std::min<int64_t>(std::max<int64_t>((chunks + per_wg - 1) / per_wg, 1), 16384);
-  if (p->dtype == FO_BF16)
-    hipLaunchKernelGGL((consume_kernel<__bf16, kUnroll, true>), dim3(grid), dim3(kThreads), 0, s, cp);
-  else
-    hipLaunchKernelGGL((consume_kernel<_Float16, kUnroll, true>), dim3(grid), dim3(kThreads), 0, s, cp);
+  launch_form<true>(p, cp, grid, s);
   return hipGetLastError() == hipSuccess ? FO_OK : FO_ERR_HIP;
 }
 

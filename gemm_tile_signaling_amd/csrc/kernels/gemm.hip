@@ -20,20 +20,23 @@
 //     per SIMD with a 64 x 64 sub-tile each (200 registers a wave), so that
 //     while one wave waits on its LDS reads or the slice barrier the other
 //     keeps the matrix pipe busy, and 112 registers per SIMD stay free for
-//     the consumer's waves.  Sub-tiles are made of 32 x 32 blocks computed
+//     the consumer's waves; the 256 x 256 tile runs 8 waves in a 2 x 4 grid,
+//     128 x 64 each (232 registers a wave, 48 per SIMD left for a small
+//     wave beside them).  Sub-tiles are made of 32 x 32 blocks computed
 //     with v_mfma_f32_32x32x16.
 //     A and B fragments are passed to the MFMA swapped (B as the first
 //     operand) so that every lane ends up with 4 consecutive columns of one
 //     output row, which the epilogue writes as 8-byte pieces.
-//   * K-slices of BK = 64 (32 for the 256 x 256 tile, whose stages are twice
-//     as large): A and B K-slices go from memory straight into LDS (gfx950
-//     buffer loads with the LDS destination, 16 bytes per lane), through a
-//     ring of LDS stages (three; six for 64 x 64 tiles, which have little
-//     arithmetic per slice to hide a load behind; four half-depth stages for
-//     256 x 256): slice k+NS-1 is loaded while slice k is multiplied, its DMA
-//     instructions spread over the slice's k-steps so the wave never waits on
-//     a full memory queue with the matrix pipe idle; no VGPRs or ds_write
-//     instructions are spent on staging.
+//   * K-slices of BK = 64: A and B K-slices go from memory straight into LDS
+//     (gfx950 buffer loads with the LDS destination, 16 bytes per lane),
+//     through a ring of LDS stages (three; six for 64 x 64 tiles, which have
+//     little arithmetic per slice to hide a load behind; two 64 KiB stages
+//     for 256 x 256, whose slice holds enough arithmetic to cover the next
+//     slice's loads): slice k+NS-1 is loaded while slice k is multiplied, its
+//     DMA instructions spread over the slice's k-steps (with two stages, all
+//     at its start, so they have the whole slice to land) so the wave never
+//     waits on a full memory queue with the matrix pipe idle; no VGPRs or
+//     ds_write instructions are spent on staging.
 //   * LDS rows are BK * 2 bytes; 16-byte chunk c of row r is stored at chunk
 //     c ^ ((r / WR) % CHUNKS), WR rows sharing one 256-byte window of the 64
 //     banks (BK = 64: c ^ ((r / 2) % 8)).  gfx950's LDS serves 16 lanes of a
@@ -42,8 +45,9 @@
 //     64 banks.  A DMA load writes lane l's 16 bytes at position l of the
 //     wave's 1 KiB destination, so each lane fetches the global chunk that
 //     belongs at its position.
-//   * The MFMA accumulators live in the accumulation registers (AGPRs); the
-//     LDS reads of k-step s+1 are issued between the MFMAs of k-step s.
+//   * The MFMA accumulators live in the accumulation registers (AGPRs),
+//     except on the 256 x 256 tile (below); the LDS reads of k-step s+1 are
+//     issued between the MFMAs of k-step s.
 //   * Each wave waits for its own loads of slice k, then the workgroup meets
 //     at a bare barrier (no memory-model fence, which would drain every
 //     outstanding load); compiler-only fences keep LDS accesses on their side
@@ -252,8 +256,8 @@ __device__ __forceinline__ bool wave_snapshot(const GemmParams &p, int w) {
   return grid_barrier(bar, status, 2u * w + 1u, p.timeout_ticks);
 }
 
-// Tile BM x BN, K-slices of BK (64 or 32) staged in LDS, NW waves per
-// workgroup (4: one per SIMD; 8: two per SIMD) in a WGM x WGN grid.
+// Tile BM x BN, K-slices of BK = 64 staged in LDS, NW waves per workgroup
+// (4: one per SIMD; 8: two per SIMD) in a WGM x WGN grid.
 template <int BM, int BN, int BK, int NW>
 struct Cfg {
   static constexpr int THREADS = 64 * NW;
@@ -266,21 +270,27 @@ struct Cfg {
   static constexpr int WR = 256 / ROWB;               // rows that share one 256-byte window of the 64 banks
   // LDS ring depth: slice k+NS-1 is loaded while slice k is multiplied.  Small
   // tiles have little arithmetic per slice, so they keep more slices in flight;
-  // half-depth slices (BK = 32) let a ring of the same size run deeper.
-  static constexpr int NS = BK == 64 ? (BM == 64 ? 6 : 3) : (BN == 256 ? 4 : 6);
+  // two 64 KiB stages of the 256 x 256 tile fill the LDS.
+  static constexpr int NS = BM == 64 ? 6 : (BM == 256 && BN == 256 ? 2 : 3);
+  // Accumulators in ordinary VGPRs (the 256 x 256 tile): with two waves per
+  // SIMD a wave has 256 registers, which in the accumulation-register form the
+  // compiler splits evenly (128 accumulators + 128 others, and spills); in the
+  // VGPR form its 128 accumulators and the rest share one budget.
+  static constexpr bool VGPR_ACC = BM == 256 && BN == 256;
   static constexpr int DIST = NS - 1;                 // prefetch distance in slices
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_PER_T = BM * CHUNKS / THREADS;  // 16-byte chunks per thread per stage
   static constexpr int B_PER_T = BN * CHUNKS / THREADS;
   static constexpr int LOADS = A_PER_T + B_PER_T;     // DMA instructions per thread per stage
-  static constexpr int DPB = (LOADS + KS - 1) / KS;   // of them issued per k-step (fewer in the last parts)
+  // of them issued per k-step (fewer in the last parts); with two stages, all in the first
+  static constexpr int DPB = NS == 2 ? LOADS : (LOADS + KS - 1) / KS;
   static constexpr int STAGE = (BM + BN) * ROWB;
   static constexpr int OUT_PITCH = BN * 2 + 16;      // bytes per staged output row
   static constexpr int OUT_BYTES = BM * OUT_PITCH;
   static constexpr int ROWOFF = OUT_BYTES;           // int64 per row after the staging tile
   static constexpr int LDS = (NS * STAGE > OUT_BYTES + BM * 8) ? NS * STAGE : OUT_BYTES + BM * 8;
-  static_assert(BK == 64 || BK == 32, "slice depth");
+  static_assert(BK == 64, "slice depth");
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
   static_assert(BM * CHUNKS % THREADS == 0 && BN * CHUNKS % THREADS == 0, "chunk split");
   static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
@@ -316,9 +326,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // Naming an accumulation register here lets the compiler give the MFMAs
   // their accumulation-register form, so the accumulators live outside the
-  // 256 architectural VGPRs that the operands, offsets and addresses need.
+  // 256 architectural VGPRs that the operands, offsets and addresses need
+  // (not with VGPR_ACC: 232 registers in one budget, no spills, against
+  // 128 + 128 and spills in the split form).
 #if defined(__HIP_DEVICE_COMPILE__)  // the register name exists only for the GPU target
-  asm volatile("; accumulators in AGPRs" ::: "a0");
+  if constexpr (!C::VGPR_ACC) asm volatile("; accumulators in AGPRs" ::: "a0");
 #endif
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -333,7 +345,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
   // chunk c ^ ((r / WR) % CHUNKS), WR rows filling one 256-byte window of the
   // 64 banks: the 16 lanes a ds_read_b128 serves per cycle read one logical
   // chunk of 16 consecutive rows, which this spreads over all 64 banks (BK = 64:
-  // 2 rows per window, XOR over 8 chunks; BK = 32: 4 rows, XOR over 4 chunks).
+  // 2 rows per window, XOR over 8 chunks).
   // global -> LDS coordinates.  DMA instruction i of wave w fills 1 KiB of
   // LDS: rows (NW i + w) * RPK .. + RPK of the operand.  Lane l lands at
   // physical chunk l % CHUNKS of row r = (NW i + w) * RPK + l / CHUNKS, which
@@ -652,7 +664,7 @@ int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
 
 template <typename T, bool SIGNAL, bool SERIAL>
 int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
-  if (p->BM == 256 && p->BN == 256) return launch_typed<T, 256, 256, 32, 4, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 256 && p->BN == 256) return launch_typed<T, 256, 256, 64, 8, SIGNAL, SERIAL>(p, gp, s);
   if (p->BM == 256 && p->BN == 128) {
     // two waves share each SIMD: on a tile with an empty 64-row or 64-column
     // band, the band's waves skipping their MFMAs lets the other wave of each

@@ -332,11 +332,10 @@ int fo_gemm_plain(const fo_plan *plan, const void *A, const void *B, void *C, hi
  *      most 96 registers and no LDS to speak of, so one consumer workgroup per
  *      CU fits beside the GEMM and two do not: a grid above the CU count could
  *      keep GEMM workgroups from being dispatched until the consumer times
- *      out.  A 256x256 workgroup takes all 512 registers, so nothing fits
- *      beside it: do not pair this consumer with that tile.
- *      fo_consume_group_gated has no such condition (with the 256x256 tile a
- *      stream-wait wave dispatched ahead of the GEMM still delays one GEMM
- *      workgroup until another one ends: correct, but slow).
+ *      out.  A 256x256 workgroup holds 464 registers per lane of every SIMD
+ *      (two 232-register waves) and 134 KiB of LDS; with such a plan the
+ *      consumer runs in a slim form of at most 48 registers, which fits the
+ *      rest.  fo_consume_group_gated uses the same forms.
  * timeout_us: upper bound on any one wait (0 = 2 s).  A workgroup that
  *      waits longer stores FO_ERR_TIMEOUT into *dev_status (if it was still
  *      0) and every workgroup then stops; later spans are left untouched.

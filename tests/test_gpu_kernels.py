@@ -196,13 +196,14 @@ def test_consumer_times_out_on_unsignalled_group_and_leaves_it_untouched():
     assert np.all(got[spans[2]:] == 0x7FC0)
 
 
-@pytest.mark.parametrize("tile,M,N", [((64, 64), 1024, 2048), ((128, 128), 2048, 4096), ((256, 128), 2048, 8192)])
+@pytest.mark.parametrize("tile,M,N", [((64, 64), 1024, 2048), ((128, 128), 2048, 4096), ((256, 128), 2048, 8192),
+                                      ((256, 256), 4096, 8192)])
 def test_polling_consumer_launched_first_stays_beside_the_gemm(tile, M, N):
     """Residency: the persistent consumer (one workgroup per CU) is launched before the GEMM on another
     queue and polls until the GEMM signals; a full wave of GEMM workgroups (W = the CU count, two waves)
     must still find room beside it on every CU, or the consumer times out (bounded at 0.5 s) before the
-    GEMM can signal.  Every tile the polling consumer serves is checked (the 256 x 256 tile takes the
-    whole register file and is documented not to be paired with it)."""
+    GEMM can signal.  Every tile is checked; beside the 256 x 256 tile (two 232-register GEMM waves per
+    SIMD) the consumer runs in its slim form."""
     K = 512
     BM, BN = tile
     p = fo.Plan([M], N, K, "bf16", BM=BM, BN=BN)     # W = the CU count, one group per wave
