@@ -662,20 +662,24 @@ int launch_typed(const fo_plan *pl, const GemmParams &gp, hipStream_t s) {
   }
 }
 
+template <typename T, int BM, int BN, bool SIGNAL, bool SERIAL>
+int launch_8wave(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
+  using C8 = Cfg<BM, BN, 64, 8>;
+  if constexpr (!SERIAL) {
+    if (p->min_tile_rows <= BM - C8::WM || p->min_tile_cols <= BN - C8::WN)
+      return launch_typed<T, BM, BN, 64, 8, SIGNAL, SERIAL, true>(p, gp, s);
+  }
+  return launch_typed<T, BM, BN, 64, 8, SIGNAL, SERIAL>(p, gp, s);
+}
+
 template <typename T, bool SIGNAL, bool SERIAL>
 int launch_tile(const fo_plan *p, const GemmParams &gp, hipStream_t s) {
-  if (p->BM == 256 && p->BN == 256) return launch_typed<T, 256, 256, 64, 8, SIGNAL, SERIAL>(p, gp, s);
-  if (p->BM == 256 && p->BN == 128) {
-    // two waves share each SIMD: on a tile with an empty 64-row or 64-column
-    // band, the band's waves skipping their MFMAs lets the other wave of each
-    // pair run alone (only the 8-wave layout gains from it)
-    using C8 = Cfg<256, 128, 64, 8>;
-    if constexpr (!SERIAL) {
-      if (p->min_tile_rows <= 256 - C8::WM || p->min_tile_cols <= 128 - C8::WN)
-        return launch_typed<T, 256, 128, 64, 8, SIGNAL, SERIAL, true>(p, gp, s);
-    }
-    return launch_typed<T, 256, 128, 64, 8, SIGNAL, SERIAL>(p, gp, s);
-  }
+  // The eight-wave tiles share each SIMD between two waves: on a plan with a
+  // tile whose wave band (rows or columns) lies wholly past its edge, the
+  // band's waves skipping their MFMAs lets the other wave of each pair run
+  // alone (the four-wave tiles, one wave per SIMD, gain nothing from it).
+  if (p->BM == 256 && p->BN == 256) return launch_8wave<T, 256, 256, SIGNAL, SERIAL>(p, gp, s);
+  if (p->BM == 256 && p->BN == 128) return launch_8wave<T, 256, 128, SIGNAL, SERIAL>(p, gp, s);
   if (p->BM == 128 && p->BN == 128) return launch_typed<T, 128, 128, 64, 4, SIGNAL, SERIAL>(p, gp, s);
   if (p->BM == 64 && p->BN == 64) return launch_typed<T, 64, 64, 64, 4, SIGNAL, SERIAL>(p, gp, s);
   return FO_ERR_UNSUPPORTED;

@@ -45,6 +45,9 @@ PLANS = [
     ("ragged_256x256", [600], 640, 192, "bf16", 256, 256, 2, 3, None, "tile", 1),
     ("subtile_r8_256x256", [512], 512, 128, "bf16", 256, 256, 1, 2, None, "subtile", 8),
     ("fp16_256x256", [256, 256], 512, 256, "fp16", 256, 256, 1, 3, (1, 1), "tile", 1),
+    # 256 x 256 tiles with a 128-row or 64-column wave band wholly past the edge (rows 40 and 44; a last
+    # column tile of 64 columns): those waves skip their MFMAs
+    ("empty_bands_256x256", [40, 300], 320, 192, "bf16", 256, 256, 2, 3, None, "tile", 1),
 ]
 
 
