@@ -112,12 +112,21 @@ struct Vec8<_Float16> {
 
 // SiLU with the hardware exp2 and reciprocal instructions: both are within a
 // few fp32 ulps, far below half an ulp of the 16-bit result, and they keep the
-// pass bound by memory rather than by the vector ALU.  exp2 overflows to +inf
-// for very negative x, whose reciprocal is 0: the result is -0, as x / inf.
+// pass bound by memory rather than by the vector ALU.  Below x = -64, e^-x
+// heads for fp32 overflow and the logistic e^x / (1 + e^x) -- equal to e^x
+// there to 2^-92 -- for the denormal range, which those instructions flush
+// to zero; so x e^x is formed at a scale of 2^64 (e^x 2^64 stays normal down
+// to x = -132) and scaled back with one multiply, exact or correctly rounded
+// into the denormals that a bf16 result can still hold (x = -inf gives NaN,
+// as x / (1 + e^-x) does).
 template <int ACT>
 __device__ __forceinline__ float act(float x) {
+  constexpr float kLog2e = 1.4426950408889634f;
   if (ACT == FO_ACT_RELU) return x > 0.0f ? x : 0.0f;
-  if (ACT == FO_ACT_SILU) return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+  if (ACT == FO_ACT_SILU) {
+    if (x > -64.0f) return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+    return (x * __builtin_amdgcn_exp2f(x * kLog2e + 64.0f)) * 0x1p-64f;
+  }
   return x;
 }
 

@@ -153,6 +153,34 @@ def test_post_reorder_epilogue(entry, act):
             assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_silu_epilogue_over_the_whole_input_range(dt):
+    """SiLU through the fused post-reorder on values spread over every exponent, negative ones included down to
+    where the logistic underflows fp32 (x < -87) and the result is a bf16 denormal or zero, plus both infinities
+    and the extreme finite values: within one unit in the last place of the fp64 oracle everywhere, NaN where
+    the oracle's formula gives NaN (x = -inf)."""
+    o, p = _plans(PLANS[0][:4] + (dt,) + PLANS[0][5:])      # the tiny plan, in the dtype under test
+    off = element_offsets(o)
+    n = o.M * o.N
+    special = np.array([-64.0, -63.99, -87.0, -88.7, -92.0, -96.0, -100.0, -103.0, -110.0, -130.0, -1e30, -3e38,
+                        3e38, -np.inf, np.inf, 0.0, -0.0, 1e-30, -1e-30], np.float32)
+    rng = np.random.Generator(np.random.PCG64(5))
+    spread = (rng.choice([-1.0, 1.0], n) * np.exp2(rng.uniform(-130, 128, n))).astype(np.float32)
+    grid = -np.linspace(0.0, 140.0, n // 4, dtype=np.float32)
+    vals = np.concatenate([special, grid, spread])[:n]
+    Y = to_bits(vals, dt)
+    want = post_epilogue(Y, off, dt, "silu", None, row_problems(o)).ravel()
+    say(f"silu over the whole range {dt}")
+    out = empty16(n)
+    p.reorder_post_ep(to_dev(Y), out, act="silu")
+    torch.cuda.synchronize()
+    got = to_host(out)
+    nan = np.isnan(oracle.decode_bits(want, dt))          # -inf: x / (1 + e^-x) is -inf / inf on both sides
+    assert np.array_equal(np.isnan(oracle.decode_bits(got, dt)), nan) and nan.any()
+    d = ulp_distance(got[~nan], want[~nan])
+    assert d.max() <= 1, (int(d.max()), int((d > 0).sum()))
+
+
 # --------------------------------------------------------------------------- consumer
 
 @pytest.mark.parametrize("entry", PLANS, ids=[e[0] for e in PLANS])

@@ -7,9 +7,10 @@ composition of the waves, K of 64 .. 256, bf16 or fp16 -- so that an indexing
 slip that only some shape exposes has many chances to show.  Inputs are
 ternary, so every product and sum of the GEMM is an exact integer and its
 16-bit output is exact: the plain GEMM's row-major C, the signaling GEMM's
-reordered buffer, the consumer's recv (a random peer, one fp32 add and one
+reordered buffer, the consumer's recv (either form; a random peer, one fp32 add and one
 rounding per element) and the post-reorder's output are all compared bit for
-bit, and the counting table and flags checked.
+bit, the fused bias + activation epilogue too (SiLU within one unit in the
+last place), and the counting table and flags checked.
 """
 
 import numpy as np
@@ -19,7 +20,9 @@ hyp = pytest.importorskip("hypothesis")
 from hypothesis import given, settings, strategies as st  # noqa: E402
 
 import oracle  # noqa: E402
-from tests.gpu_util import empty16, say, to_dev, to_host, zeros_i32  # noqa: E402
+from oracle.epilogue import post_epilogue, row_problems  # noqa: E402
+from oracle.layout import element_offsets  # noqa: E402
+from tests.gpu_util import empty16, say, to_dev, to_host, ulp_distance, zeros_i32  # noqa: E402
 from tests.test_properties import _oracle_plan, plans  # noqa: E402
 from workloads import draw, random_bits, to_bits  # noqa: E402
 
@@ -30,8 +33,9 @@ torch = pytest.importorskip("torch")
 
 
 @settings(max_examples=150, deadline=None, derandomize=True, database=None)
-@given(plans(), st.sampled_from(["bf16", "fp16"]), st.integers(1, 4), st.integers(0, 2 ** 16))
-def test_kernels_on_random_plans(c, dtype, kq, seed):
+@given(plans(), st.sampled_from(["bf16", "fp16"]), st.integers(1, 4), st.integers(0, 2 ** 16),
+       st.sampled_from(["gated", "poll"]), st.sampled_from(["none", "relu", "silu"]))
+def test_kernels_on_random_plans(c, dtype, kq, seed, consumer, act):
     K = 64 * kq
     o = _oracle_plan(c)
     M, N = o.M, o.N
@@ -43,21 +47,32 @@ def test_kernels_on_random_plans(c, dtype, kq, seed):
                 mode=c["mode"], ranks=c["ranks"], row_dest=c["row_dest"])
     try:
         say(f"random plan {c['mode']} m={c['m']} N={N} K={K} {c['BM']}x{c['BN']} S={c['S']} W={c['W']} "
-            f"comp={c['comp']} {dtype} NT={p.NT} P={p.P}")
+            f"comp={c['comp']} {dtype} NT={p.NT} P={p.P} consumer={consumer} act={act}")
         dA, dB, dpeer = to_dev(A), to_dev(np.concatenate([b.reshape(-1) for b in B])), to_dev(peer)
-        C, buf, recv, out = (empty16(M * N) for _ in range(4))
+        C, buf, recv, out, out_ep = (empty16(M * N) for _ in range(5))
+        bias = to_bits(draw(seed + 4, (len(c["m"]) * N,), ("normal", 1.0)), dtype)
         sig = p.new_sig()
         status = zeros_i32(1)
         p.gemm_plain(dA, dB, C)
         p.gemm_signal(dA, dB, buf, sig, 1)
-        p.consume_group_gated(buf, dpeer, recv, sig, 1, status)
+        if consumer == "gated":
+            p.consume_group_gated(buf, dpeer, recv, sig, 1, status)
+        else:
+            p.consume_group(buf, dpeer, recv, sig, 1, status)
         p.reorder_post(recv, out)
+        p.reorder_post_ep(recv, out_ep, bias=to_dev(bias), act=act)
         torch.cuda.synchronize()
         assert int(status.item()) == 0
         assert np.array_equal(to_host(C), r["C"].ravel())
         assert np.array_equal(to_host(buf), r["send"])
         assert np.array_equal(to_host(recv), r["recv"])
         assert np.array_equal(to_host(out), r["out"].ravel())
+        # the fused epilogue: bias + activation in the post-reorder's pass (SiLU within one unit in the last place)
+        want_ep = post_epilogue(r["recv"], element_offsets(o), dtype, act, bias, row_problems(o)).ravel()
+        if act == "silu":
+            assert ulp_distance(to_host(out_ep), want_ep).max() <= 1
+        else:
+            assert np.array_equal(to_host(out_ep), want_ep)
         s = sig.cpu().numpy()
         assert s[:p.P].tolist() == list(o.group_tiles)
         assert s[p.flag_offset:p.flag_offset + p.P].tolist() == [1] * p.P
