@@ -146,9 +146,11 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
     s = streams[0]
     td = {"bf16": torch.bfloat16, "fp16": torch.float16}
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    # the prefill, ReduceScatter and MoE shapes keep two or more waves with 256 x 256 tiles as well
-    runs = [("ar_prefill", None), ("ar_prefill", (256, 256)), ("ar_decode", None), ("rs", None), ("rs", (256, 256)),
-            ("moe_a2a", None), ("moe_a2a", (256, 256))]
+    # the prefill, ReduceScatter and MoE shapes keep two or more waves with 256 x 256 tiles as well; on the
+    # profiled shape that tile leaves a single wave (one group, nothing to overlap), and its line compares the
+    # GEMM with the library's on the same operands
+    runs = [("profiled", (256, 256)), ("ar_prefill", None), ("ar_prefill", (256, 256)), ("ar_decode", None),
+            ("rs", None), ("rs", (256, 256)), ("moe_a2a", None), ("moe_a2a", (256, 256))]
     for name, tile in runs:
         w = WORKLOADS[name]
         BM, BN = tile or (w.BM, w.BN)
@@ -176,17 +178,30 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
         def _sig(st):
             ep[0] += 1
             plan.gemm_signal(dA, dB, C, sig, ep[0], stream=st)
-        for _ in range(3):
-            _sig(s)
-        sig_ms, plain_ms = _time_pair(torch, _sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s, 10)
+        launches = [_sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st)]
+        if not w.experts:
+            # context only: the library GEMM (hipBLASLt through torch) on the same operands, C = A . B^T
+            a_mat = dA.view(td[w.dtype]).view(M, w.K)
+            b_mat = dB.view(td[w.dtype]).view(w.N, w.K)
+            c_mat = torch.empty(M, w.N, dtype=td[w.dtype], device=dev)
+
+            def _lib(st):
+                with torch.cuda.stream(st):
+                    torch.mm(a_mat, b_mat.t(), out=c_mat)
+            launches.append(_lib)
+        times = _time_blocks(torch, launches, s, 10)
+        sig_ms, plain_ms = times[0], times[1]
+        lib_tflops = round(flops / (times[2] * 1e-3) / 1e12, 1) if len(times) > 2 else None
+        if not w.experts:
+            del a_mat, b_mat, c_mat
         # the matrix pipe's ceiling on this workload's A values (fo_mfma_rate), after the clock settles
-        pr_out = torch.empty(n_cu * 256, dtype=torch.float32, device=dev)
+        pr_out = torch.empty(n_cu * 512, dtype=torch.float32, device=dev)
 
         def _rate(st):
-            fo.mfma_rate(dA, pr_out, n_cu, 1280, dtype=w.dtype, stream=st)
+            fo.mfma_rate(dA, pr_out, n_cu, 320, dtype=w.dtype, stream=st)
         for _ in range(200):
             _rate(s)
-        rate_tflops = fo.mfma_rate_flops(n_cu, 1280) / (_time_kernel(torch, _rate, s, 20) * 1e-3) / 1e12
+        rate_tflops = fo.mfma_rate_flops(n_cu, 320) / (_time_kernel(torch, _rate, s, 20) * 1e-3) / 1e12
         del pr_out
         # the schedule: gated or polling consumer, post-reorder per group or whole, chosen from
         # interleaved blocks of passes as for the headline
@@ -238,6 +253,7 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
                "signal_in_pass_over_plain": round(plain_ms / gemm_pipe_ms, 4),
                "frac_of_peak": round(flops / (gemm_pipe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                "mfma_rate_workload_operands_tflops": round(rate_tflops, 1),
+               "context_library_gemm_tflops": lib_tflops,
                # which roof bounds this shape: its arithmetic intensity (FLOP per algorithmic HBM byte:
                # A, every problem's B and C once each) against the ridge of the two peaks
                "flop_per_byte": round(flops / alg_bytes, 1),
@@ -358,14 +374,18 @@ def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
     }
 
 
-def _time_pair(torch, launch_a, launch_b, stream, n, rounds=3):
-    """Average durations (ms) of two launches timed in alternating blocks of n (median block of each over
-    `rounds` rounds), so that clock and power drift falls on both alike."""
-    a, b = [], []
+def _time_blocks(torch, launches, stream, n, rounds=3, warmup=30):
+    """Average durations (ms) of several launches timed in alternating blocks of n (median block of each over
+    `rounds` rounds), after `warmup` untimed launches of each in turn, so that the clock has settled under
+    their load and drift falls on all alike (a kernel timed first after lighter work ran up to 15% slower)."""
+    for _ in range(warmup):
+        for f in launches:
+            f(stream)
+    t = [[] for _ in launches]
     for _ in range(rounds):
-        a.append(_time_kernel(torch, launch_a, stream, n))
-        b.append(_time_kernel(torch, launch_b, stream, n))
-    return float(np.median(a)), float(np.median(b))
+        for i, f in enumerate(launches):
+            t[i].append(_time_kernel(torch, f, stream, n))
+    return [float(np.median(x)) for x in t]
 
 
 def _time_kernel(torch, launch, stream, n, scratch=None):
@@ -689,8 +709,18 @@ def main():
     def _sig(st):
         ep[0] += 1
         plan.gemm_signal(dA, dB, pipe.buf, sig, ep[0], stream=st)
-    signal_ms, plain_ms = _time_pair(torch, _sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st), s,
-                                     max(10, n_alone // 3))
+    # context only: the library GEMM (hipBLASLt through torch) on the same operands, C = A . B^T, timed in
+    # the same alternating blocks as the two GEMMs
+    a_mat = dA.view(torch.bfloat16 if w.dtype == "bf16" else torch.float16).view(w.M, w.K)
+    b_mat = dB.view(a_mat.dtype).view(w.N, w.K)
+    c_mat = torch.empty(w.M, w.N, dtype=a_mat.dtype, device=dev)
+
+    def _lib(st):
+        with torch.cuda.stream(st):
+            torch.mm(a_mat, b_mat.t(), out=c_mat)
+    signal_ms, plain_ms, lib_ms = _time_blocks(torch, [_sig, lambda st: plan.gemm_plain(dA, dB, C, stream=st), _lib],
+                                               s, max(10, n_alone // 3))
+    del c_mat
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     ready = plan.new_sig(dev)
     plan.flag_of(ready).fill_(1)
@@ -724,26 +754,13 @@ def main():
         _add(s)
     add_ms = _time_kernel(torch, _add, s, n_alone, scratch)
     del cp_src, add_a, add_b, add_c
-    # context only: the library GEMM (hipBLASLt through torch) on the same operands, C = A . B^T
-    a_mat = dA.view(torch.bfloat16 if w.dtype == "bf16" else torch.float16).view(w.M, w.K)
-    b_mat = dB.view(a_mat.dtype).view(w.N, w.K)
-    c_mat = torch.empty(w.M, w.N, dtype=a_mat.dtype, device=dev)
-
-    def _lib(st):
-        with torch.cuda.stream(st):
-            torch.mm(a_mat, b_mat.t(), out=c_mat)
-    for _ in range(3):
-        _lib(s)
-    torch.cuda.synchronize()
-    lib_ms = _time_kernel(torch, _lib, s, n_alone)
-    del c_mat
-    # the matrix pipe's ceiling on this data (fo_mfma_rate: MFMAs only, no loads, LDS or epilogue), one
-    # workgroup of four waves per CU, on operand values read from A (the GEMM's own distribution) and on
-    # zeros (no multiplier toggles); each after 200 untimed launches of about the GEMM's length, so the
-    # clock has settled under that load
+    # the matrix pipe's ceiling on this data (fo_mfma_rate: the 256 x 128 tile's MFMAs only, no loads, LDS
+    # or epilogue; one workgroup of eight waves per CU), on operand values read from A (the GEMM's own
+    # distribution) and on zeros (no multiplier toggles); each after 200 untimed launches of about the GEMM's
+    # length, so the clock has settled under that load
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    pr_iters = 1280
-    pr_out = torch.empty(n_cu * 256, dtype=torch.float32, device=dev)
+    pr_iters = 320
+    pr_out = torch.empty(n_cu * 512, dtype=torch.float32, device=dev)
     pr_zero = torch.zeros(4096, dtype=torch.int16, device=dev)
     mfma_rate = {}
     for key, ops in (("workload_operands_tflops", dA), ("zero_operands_tflops", pr_zero)):

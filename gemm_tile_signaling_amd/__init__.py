@@ -175,18 +175,18 @@ def stream_destroy(s):
 
 def mfma_rate(ops, out, workgroups: int, iters: int, dtype: str = "bf16", stream=None):
     """``fo_mfma_rate``: MFMAs only, on operand values read from ``ops`` (a measurement aid for the GEMM's
-    roofline).  ``out``: float32 device tensor of ``workgroups * 256`` elements."""
+    roofline).  ``out``: float32 device tensor of ``workgroups * 512`` elements."""
     nbytes = ops.numel() * ops.element_size() if hasattr(ops, "numel") else None
     if nbytes is None:
         raise TypeError("ops: expected a device tensor")
     _check(lib().fo_mfma_rate(_DTYPES[dtype], _ptr(ops, name="ops"), nbytes, int(workgroups), int(iters),
-                              _ptr(out, numel=int(workgroups) * 256, itemsize=4, name="out"), _stream(stream)),
+                              _ptr(out, numel=int(workgroups) * 512, itemsize=4, name="out"), _stream(stream)),
            "fo_mfma_rate")
 
 
 def mfma_rate_flops(workgroups: int, iters: int) -> float:
-    """FLOP of one ``mfma_rate`` launch: 4 waves x ``iters`` rounds x 8 MFMAs of 32x32x16 per workgroup."""
-    return float(workgroups) * 4 * iters * 8 * 2 * 32 * 32 * 16
+    """FLOP of one ``mfma_rate`` launch: 8 waves x ``iters`` rounds x 32 MFMAs of 16x16x32 per workgroup."""
+    return float(workgroups) * 8 * iters * 32 * 2 * 16 * 16 * 32
 
 
 class Plan:

@@ -17,13 +17,14 @@
 //     inside a wave.
 //   * 4 waves in a 2 x 2 grid, one per SIMD, each owning a (BM/2) x (BN/2)
 //     sub-tile; the 256 x 128 tile runs 8 waves in a 4 x 2 grid instead, two
-//     per SIMD with a 64 x 64 sub-tile each (200 registers a wave), so that
+//     per SIMD with a 64 x 64 sub-tile each (192 registers a wave), so that
 //     while one wave waits on its LDS reads or the slice barrier the other
-//     keeps the matrix pipe busy, and 112 registers per SIMD stay free for
+//     keeps the matrix pipe busy, and 128 registers per SIMD stay free for
 //     the consumer's waves; the 256 x 256 tile runs 8 waves in a 2 x 4 grid,
 //     128 x 64 each (232 registers a wave, 48 per SIMD left for a small
-//     wave beside them).  Sub-tiles are made of 32 x 32 blocks computed
-//     with v_mfma_f32_32x32x16.
+//     wave beside them).  Sub-tiles are made of 16 x 16 blocks computed
+//     with v_mfma_f32_16x16x32 on the 256 x 128 tile, of 32 x 32 blocks
+//     computed with v_mfma_f32_32x32x16 elsewhere.
 //     A and B fragments are passed to the MFMA swapped (B as the first
 //     operand) so that every lane ends up with 4 consecutive columns of one
 //     output row, which the epilogue writes as 8-byte pieces.
@@ -45,9 +46,10 @@
 //     64 banks.  A DMA load writes lane l's 16 bytes at position l of the
 //     wave's 1 KiB destination, so each lane fetches the global chunk that
 //     belongs at its position.
-//   * The MFMA accumulators live in the accumulation registers (AGPRs),
-//     except on the 256 x 256 tile (below); the LDS reads of k-step s+1 are
-//     issued between the MFMAs of k-step s.
+//   * The MFMA accumulators live in the accumulation registers (AGPRs) on
+//     the four-wave tiles and in ordinary VGPRs on the eight-wave ones
+//     (below); the LDS reads of k-step s+1 are issued between the MFMAs of
+//     k-step s.
 //   * Each wave waits for its own loads of slice k, then the workgroup meets
 //     at a bare barrier (no memory-model fence, which would drain every
 //     outstanding load); compiler-only fences keep LDS accesses on their side
@@ -124,16 +126,36 @@ __device__ __forceinline__ void bare_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename T>
-__device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c);
+// One MFMA on an MB x MB output block: v_mfma_f32_32x32x16 (MB = 32, 16 fp32
+// results per lane) or v_mfma_f32_16x16x32 (MB = 16, 4 per lane); both take
+// 8 16-bit values of K per lane and operand.
+template <int MB>
+struct Acc;
 template <>
-__device__ __forceinline__ f32x16 mma<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
+struct Acc<32> { typedef f32x16 type; };
+template <>
+struct Acc<16> { typedef f32x4 type; };
+
+template <typename T, int MB>
+__device__ __forceinline__ typename Acc<MB>::type mma(u32x4 a, u32x4 b, typename Acc<MB>::type c);
+template <>
+__device__ __forceinline__ f32x16 mma<__bf16, 32>(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 template <>
-__device__ __forceinline__ f32x16 mma<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mma<_Float16, 32>(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mma<__bf16, 16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mma<_Float16, 16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                 0, 0);
 }
 
@@ -265,21 +287,34 @@ struct Cfg {
   static constexpr int WGN = NW / WGM;
   static constexpr int ROWB = BK * 2;                 // bytes of one staged row of A or B
   static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per staged row
-  static constexpr int KS = BK / 16;                  // MFMA k-steps per slice
+  // MFMA block: 16 x 16 x 32 on the 256 x 128 tile -- under the power cap the
+  // matrix pipe sustains about 13% more FLOP/s with it than with 32 x 32 x 16
+  // on the same values when two waves share a SIMD, each with a 4 x 4 block
+  // grid (the tile ran 9-11% faster) -- and 32 x 32 x 16 elsewhere: one wave
+  // per SIMD (the four-wave tiles) leaves the smaller instruction's
+  // accumulation chains too short to cover its latency (the 128 x 128 tile
+  // ran 16% slower with it), and on the 256 x 256 tile the fragments of two
+  // k-steps of 16 x 16 blocks take twice the registers: a wave would hold all
+  // 256, leaving no room on the SIMD for another wave beside the GEMM.
+  static constexpr int MB = NW == 8 && BN == 128 ? 16 : 32;
+  static constexpr int LG = 64 / MB;                  // lane groups: lanes l, l + MB, ... hold successive K-chunks
+  static constexpr int KS = BK / (8 * LG);            // MFMA k-steps per slice (each 8 * LG deep)
+  static constexpr int GPB = MB * MB / 256;           // groups of 4 output columns a lane holds per block
   static constexpr int RPK = 1024 / ROWB;             // staged rows per KiB (one DMA instruction of a wave)
   static constexpr int WR = 256 / ROWB;               // rows that share one 256-byte window of the 64 banks
   // LDS ring depth: slice k+NS-1 is loaded while slice k is multiplied.  Small
   // tiles have little arithmetic per slice, so they keep more slices in flight;
   // two 64 KiB stages of the 256 x 256 tile fill the LDS.
   static constexpr int NS = BM == 64 ? 6 : (BM == 256 && BN == 256 ? 2 : 3);
-  // Accumulators in ordinary VGPRs (the 256 x 256 tile): with two waves per
+  // Accumulators in ordinary VGPRs (the eight-wave tiles): with two waves per
   // SIMD a wave has 256 registers, which in the accumulation-register form the
-  // compiler splits evenly (128 accumulators + 128 others, and spills); in the
-  // VGPR form its 128 accumulators and the rest share one budget.
-  static constexpr bool VGPR_ACC = BM == 256 && BN == 256;
+  // compiler splits evenly (accumulators + the rest, each at most 128: the
+  // fragments then spilled into the accumulation registers, or to memory); in
+  // the VGPR form the accumulators and the rest share one budget.
+  static constexpr bool VGPR_ACC = NW == 8;
   static constexpr int DIST = NS - 1;                 // prefetch distance in slices
   static constexpr int WM = BM / WGM, WN = BN / WGN;
-  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int FM = WM / MB, FN = WN / MB;
   static constexpr int A_PER_T = BM * CHUNKS / THREADS;  // 16-byte chunks per thread per stage
   static constexpr int B_PER_T = BN * CHUNKS / THREADS;
   static constexpr int LOADS = A_PER_T + B_PER_T;     // DMA instructions per thread per stage
@@ -293,7 +328,7 @@ struct Cfg {
   static_assert(BK == 64, "slice depth");
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
   static_assert(BM * CHUNKS % THREADS == 0 && BN * CHUNKS % THREADS == 0, "chunk split");
-  static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(FM >= 1 && FN >= 1 && WM % MB == 0 && WN % MB == 0, "wave tile");
   static_assert(NS * LOADS <= 63, "loads in flight fit the vmcnt counter");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
@@ -357,9 +392,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
   const uint32_t g_step = (uint32_t)NW * C::RPK * row_bytes;
   static_assert((NW * C::RPK / C::WR) % C::CHUNKS == 0, "the swizzle repeats every NW RPK rows");
   constexpr uint32_t s_bofs = BM * kRowBytes;      // B rows follow A rows in a stage
-  // MFMA fragment reads: row (lane % 32) of each 32-row block, K-chunk ks*2 + lane/32
-  const int frag_row = lane & 31, frag_half = lane >> 5, swz = (frag_row / C::WR) % C::CHUNKS;
-  static_assert((32 / C::WR) % C::CHUNKS == 0, "every 32-row block has the same swizzle");
+  // MFMA fragment reads: row (lane % MB) of each MB-row block, K-chunk ks * LG + lane / MB
+  const int frag_row = lane % C::MB, frag_g = lane / C::MB, swz = (frag_row / C::WR) % C::CHUNKS;
+  static_assert((C::MB / C::WR) % C::CHUNKS == 0, "every block of MB rows has the same swizzle");
   const uint32_t a_frag = (uint32_t)((wm * C::WM + frag_row) * kRowBytes);
   const uint32_t b_frag = (uint32_t)(s_bofs + (wn * C::WN + frag_row) * kRowBytes);
 
@@ -403,31 +438,31 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
       continue;
     }
 
-    f32x16 acc[C::FM][C::FN];
+    typename Acc<C::MB>::type acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = typename Acc<C::MB>::type{};
 
-    // Fragments of one 16-deep k-step of a stage, into register set u, read
+    // Fragments of one k-step of a stage, into register set u, read
     // in the order the MFMAs below consume them.
     u32x4 fa[2][C::FM], fb[2][C::FN];
     auto read_frags = [&](int u, int stage, int ks) {
       const char *base = smem + (stage % C::NS) * C::STAGE;
-      const uint32_t chunk = (uint32_t)(((ks * 2 + frag_half) ^ swz) << 4);
+      const uint32_t chunk = (uint32_t)(((ks * C::LG + frag_g) ^ swz) << 4);
       fa[u][0] = *reinterpret_cast<const u32x4 *>(base + a_frag + chunk);
 #pragma unroll
       for (int f = 0; f < C::FN; ++f)
-        fb[u][f] = *reinterpret_cast<const u32x4 *>(base + b_frag + f * 32 * kRowBytes + chunk);
+        fb[u][f] = *reinterpret_cast<const u32x4 *>(base + b_frag + f * C::MB * kRowBytes + chunk);
 #pragma unroll
       for (int f = 1; f < C::FM; ++f)
-        fa[u][f] = *reinterpret_cast<const u32x4 *>(base + a_frag + f * 32 * kRowBytes + chunk);
+        fa[u][f] = *reinterpret_cast<const u32x4 *>(base + a_frag + f * C::MB * kRowBytes + chunk);
     };
     auto mfmas = [&](int u) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = mma<T>(fb[u][j], fa[u][i], acc[i][j]);
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mma<T, C::MB>(fb[u][j], fa[u][i], acc[i][j]);
     };
     // Order inside a block: its share of DMA loads spread out, its LDS reads
     // alternating with its MFMAs, so the wave never sits on a queue while the
@@ -560,15 +595,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmParams p) {
     // (an instruction immediate), so no per-fragment address is computed once
     // and kept in a register across tiles: on a 256 x 256 tile that alone ran
     // the VGPRs out next to 256 accumulators.
-    char *const stage_w = smem + (wm * C::WM + frag_row) * C::OUT_PITCH + (wn * C::WN + frag_half * 4) * 2;
+    // Lane l holds, of every block, row l % MB and the 4 consecutive columns
+    // g * 4 LG + 4 (l / MB) .. + 3 for each of its GPB groups g.
+    char *const stage_w = smem + (wm * C::WM + frag_row) * C::OUT_PITCH + (wn * C::WN + frag_g * 4) * 2;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
+        for (int g4 = 0; g4 < C::GPB; ++g4) {
           const f32x4 v = {acc[i][j][g4 * 4 + 0], acc[i][j][g4 * 4 + 1], acc[i][j][g4 * 4 + 2], acc[i][j][g4 * 4 + 3]};
-          *reinterpret_cast<u32x2 *>(stage_w + i * 32 * C::OUT_PITCH + (j * 32 + g4 * 8) * 2) = pack4<T>(v);
+          *reinterpret_cast<u32x2 *>(stage_w + i * C::MB * C::OUT_PITCH + (j * C::MB + g4 * 4 * C::LG) * 2) =
+              pack4<T>(v);
         }
         __builtin_amdgcn_sched_barrier(0);
       }

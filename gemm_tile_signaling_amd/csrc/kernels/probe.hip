@@ -10,36 +10,38 @@
 // GEMM's own A), so its rate is the ceiling that operand values and the power
 // cap leave for any kernel on the same data, without loads, LDS or epilogue.
 //
-// Design: 256 threads (four waves, one per SIMD) per workgroup.  Every lane
-// reads 2 * kChains 16-byte vectors from the buffer (indices wrap modulo the
-// buffer's length), then runs `iters` rounds of kChains independent
-// v_mfma_f32_32x32x16 (enough independent accumulators to cover the
-// instruction's latency), each chain with its own A and B operands, so
-// consecutive MFMAs see different values as in a GEMM.  Each lane stores the
-// sum of its accumulators, which keeps the work observable.
+// Design: the signaling GEMM's 256 x 128 tile in MFMAs alone.  512 threads
+// (eight waves, two per SIMD) per workgroup; every lane reads 16 vectors of 16
+// bytes from the buffer (indices wrap modulo the buffer's length): two sets
+// of 4 A and 4 B fragments.  Each round runs, for each set in turn, the 4 x 4
+// outer product of v_mfma_f32_16x16x32 that a wave's 64 x 64 sub-tile does per
+// k-step (B fragment first, as in the GEMM), 32 MFMAs into 16 accumulators,
+// so consecutive MFMAs share an A fragment and the operands change between
+// k-steps as in the GEMM.  Each lane stores the sum of its accumulators, which
+// keeps the work observable.
 #include "../fo_internal.h"
 
 namespace fo {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
-constexpr int kThreads = 256;
-constexpr int kChains = 8;
+constexpr int kThreads = 512;
+constexpr int kFrag = 4;  // A and B fragments per set: a 4 x 4 block grid of 16 x 16
 
 template <typename T>
-__device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c);
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c);
 template <>
-__device__ __forceinline__ f32x16 mma<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+__device__ __forceinline__ f32x4 mma<__bf16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 template <>
-__device__ __forceinline__ f32x16 mma<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+__device__ __forceinline__ f32x4 mma<_Float16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                 0, 0);
 }
 
@@ -47,24 +49,33 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const u32x4 *ops, uint64_t n_vec, int32_t iters,
                                                              float *out) {
   const uint64_t lane_id = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-  u32x4 a[kChains], b[kChains];
+  u32x4 a[2][kFrag], b[2][kFrag];
 #pragma unroll
-  for (int j = 0; j < kChains; ++j) {
-    a[j] = ops[(lane_id * 2 * kChains + j) % n_vec];
-    b[j] = ops[(lane_id * 2 * kChains + kChains + j) % n_vec];
-  }
-  f32x16 acc[kChains];
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-  for (int j = 0; j < kChains; ++j) acc[j] = f32x16{};
-  for (int32_t it = 0; it < iters; ++it) {
+    for (int j = 0; j < kFrag; ++j) {
+      a[u][j] = ops[(lane_id * 16 + u * 8 + j) % n_vec];
+      b[u][j] = ops[(lane_id * 16 + u * 8 + kFrag + j) % n_vec];
+    }
+  f32x4 acc[kFrag][kFrag];
 #pragma unroll
-    for (int j = 0; j < kChains; ++j) acc[j] = mma<T>(a[j], b[j], acc[j]);
-  }
+  for (int i = 0; i < kFrag; ++i)
+#pragma unroll
+    for (int j = 0; j < kFrag; ++j) acc[i][j] = f32x4{};
+  for (int32_t it = 0; it < iters; ++it)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < kFrag; ++i)
+#pragma unroll
+        for (int j = 0; j < kFrag; ++j) acc[i][j] = mma<T>(b[u][j], a[u][i], acc[i][j]);
   float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kChains; ++j)
+  for (int i = 0; i < kFrag; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += acc[j][r];
+    for (int j = 0; j < kFrag; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += acc[i][j][r];
   out[lane_id] = s;
 }
 

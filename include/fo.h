@@ -326,8 +326,8 @@ int fo_gemm_plain(const fo_plan *plan, const void *A, const void *B, void *C, hi
  *      the CU count, else FO_ERR_INVALID.  Residency: the consumer's
  *      workgroups wait on the CUs for flags that the GEMM raises, so the GEMM's
  *      W workgroups must still find room beside them.  A GEMM workgroup of the
- *      64x64, 128x128 or 256x128 tile holds up to 408 of a SIMD's 512
- *      registers per lane (two 204-register waves on 256x128) and 144 KiB of
+ *      64x64, 128x128 or 256x128 tile holds up to 384 of a SIMD's 512
+ *      registers per lane (two 192-register waves on 256x128) and 144 KiB of
  *      the CU's 160 KiB LDS; a consumer workgroup is one wave per SIMD of at
  *      most 96 registers and no LDS to speak of, so one consumer workgroup per
  *      CU fits beside the GEMM and two do not: a grid above the CU count could
@@ -474,18 +474,20 @@ int fo_stream_destroy(hipStream_t stream);
 /*
  * Measurement aid for the signaling GEMM's roofline, not a step of the method
  * (the pages time their GEMM against its hardware; deep-dive 三 › 调优挑战).
- * Runs nothing but v_mfma_f32_32x32x16 (dtype: fo_dtype, bf16 or fp16) on
- * operand registers read from `ops`, so its rate is the matrix pipe's ceiling
- * for those values at the clock the part keeps under the load -- without the
- * GEMM's loads, LDS traffic or epilogue.  `workgroups` workgroups of 256
- * threads (four waves, one per SIMD); every lane reads 16 vectors of 16 bytes
- * from `ops` (lane i's vectors 16i .. 16i+15, indices modulo ops_bytes / 16:
- * the first 8 are A operands, the next 8 B operands), then runs `iters` rounds
- * of 8 independent MFMAs, one per (A, B) pair, and stores the sum of its
- * accumulators in out[lane] (fp32, summed in register order).
- *   FLOP per launch = workgroups * 4 * iters * 8 * 2 * 32 * 32 * 16.
+ * Runs nothing but the MFMAs of the GEMM's 256 x 128 tile, v_mfma_f32_16x16x32
+ * (dtype: fo_dtype, bf16 or fp16), on operand registers read from `ops`, so
+ * its rate is the matrix pipe's ceiling for those values at the clock the
+ * part keeps under that load -- without the GEMM's loads, LDS traffic or
+ * epilogue.  `workgroups` workgroups of 512 threads (eight waves, two per
+ * SIMD); every lane reads 16 vectors of 16 bytes from `ops` (lane i's vectors
+ * 16i .. 16i+15, indices modulo ops_bytes / 16: two sets of 4 A operands then
+ * 4 B operands), then runs `iters` rounds; a round multiplies, for each set in
+ * turn, every (A, B) pair of the set into its own accumulator (A-major, B as
+ * the instruction's first operand: 16 MFMAs per set), and the lane stores the
+ * sum of its accumulators in out[lane] (fp32, summed in register order).
+ *   FLOP per launch = workgroups * 8 * iters * 32 * 2 * 16 * 16 * 32.
  * ops: device, 16-byte aligned, ops_bytes a positive multiple of 16; out:
- * device float[workgroups * 256]; 1 <= workgroups <= 65536; 0 <= iters.
+ * device float[workgroups * 512]; 1 <= workgroups <= 65536; 0 <= iters.
  * FO_ERR_INVALID on any other argument; FO_ERR_HIP if the launch fails.
  */
 int fo_mfma_rate(int32_t dtype, const void *ops, int64_t ops_bytes, int32_t workgroups, int32_t iters, float *out,
