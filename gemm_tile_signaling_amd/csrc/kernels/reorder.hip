@@ -112,20 +112,19 @@ struct Vec8<_Float16> {
 
 // SiLU with the hardware exp2 and reciprocal instructions: both are within a
 // few fp32 ulps, far below half an ulp of the 16-bit result, and they keep the
-// pass bound by memory rather than by the vector ALU.  Below x = -64, e^-x
-// heads for fp32 overflow and the logistic e^x / (1 + e^x) -- equal to e^x
-// there to 2^-92 -- for the denormal range, which those instructions flush
-// to zero; so x e^x is formed at a scale of 2^64 (e^x 2^64 stays normal down
-// to x = -132) and scaled back with one multiply, exact or correctly rounded
-// into the denormals that a bf16 result can still hold (x = -inf gives NaN,
-// as x / (1 + e^-x) does).
+// pass bound by memory rather than by the vector ALU.  One path for every x:
+// e = 2^64 e^-|x| (at most 2^64, and normal in fp32 down to |x| = 132, where
+// the hardware exp2 would flush e^-|x| itself to zero), and the logistic of x
+// is 2^64 / (2^64 + e) for x >= 0 and e / (2^64 + e) below, so results into
+// the bf16 denormals keep their value; x = -inf gives NaN, as x / (1 + e^-x)
+// does (-inf times a zero logistic).
 template <int ACT>
 __device__ __forceinline__ float act(float x) {
   constexpr float kLog2e = 1.4426950408889634f;
   if (ACT == FO_ACT_RELU) return x > 0.0f ? x : 0.0f;
   if (ACT == FO_ACT_SILU) {
-    if (x > -64.0f) return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
-    return (x * __builtin_amdgcn_exp2f(x * kLog2e + 64.0f)) * 0x1p-64f;
+    const float e = __builtin_amdgcn_exp2f(64.0f - __builtin_fabsf(x) * kLog2e);
+    return x * ((x >= 0.0f ? 0x1p64f : e) * __builtin_amdgcn_rcpf(0x1p64f + e));
   }
   return x;
 }
