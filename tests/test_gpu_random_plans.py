@@ -32,7 +32,7 @@ fo = pytest.importorskip("gemm_tile_signaling_amd")
 torch = pytest.importorskip("torch")
 
 
-@settings(max_examples=150, deadline=None, derandomize=True, database=None)
+@settings(max_examples=400, deadline=None, derandomize=True, database=None)
 @given(plans(), st.sampled_from(["bf16", "fp16"]), st.integers(1, 4), st.integers(0, 2 ** 16),
        st.sampled_from(["gated", "poll"]), st.sampled_from(["none", "relu", "silu"]))
 def test_kernels_on_random_plans(c, dtype, kq, seed, consumer, act):
