@@ -11,7 +11,7 @@
 //   post-communication reorder's pass, so the output is written once.
 //
 // Design: pure data movement, bound by HBM bandwidth.  One workgroup per
-// (slot, band of up to 128 tile rows), over all slots or over the slots of a
+// (slot, band of up to 256 tile rows), over all slots or over the slots of a
 // range of groups (a group's slots are consecutive); every row of a tile is a contiguous
 // run of `cols` elements on both sides, so all accesses are 16-byte buffer
 // loads and stores with 32-bit offsets (the plan keeps M*N at most 2^30).  The
@@ -247,7 +247,7 @@ void launch_post_ep_typed(const fo_plan *p, const ReorderParams &rp, hipStream_t
     hipLaunchKernelGGL((post_ep_kernel<T, 64, 32, ACT, BIAS>), dim3(p->NT, (p->BM + 63) / 64), dim3(kThreads), 0, s,
                        rp);
   else if (p->BN == 128)
-    hipLaunchKernelGGL((post_ep_kernel<T, 128, 16, ACT, BIAS>), dim3(p->NT, (p->BM + 127) / 128), dim3(kThreads), 0,
+    hipLaunchKernelGGL((post_ep_kernel<T, 256, 16, ACT, BIAS>), dim3(p->NT, (p->BM + 255) / 256), dim3(kThreads), 0,
                        s, rp);
   else
     hipLaunchKernelGGL((post_ep_kernel<T, 64, 8, ACT, BIAS>), dim3(p->NT, (p->BM + 63) / 64), dim3(kThreads), 0, s,
@@ -274,7 +274,10 @@ int launch_reorder_params(const fo_plan *p, const ReorderParams &rp, int32_t nsl
     constexpr int RPB = 64;
     hipLaunchKernelGGL((reorder_kernel<RPB, 32>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
   } else if (p->BN == 128) {
-    constexpr int RPB = 128;
+    // a whole tile of up to 256 rows per workgroup, 16 chunks in flight per
+    // thread: 5% faster than bands of 128 rows on 32 MiB (82 registers, which
+    // fit beside the 256 x 128 GEMM's two 192-register waves)
+    constexpr int RPB = 256;
     hipLaunchKernelGGL((reorder_kernel<RPB, 16>), dim3(nslots, (p->BM + RPB - 1) / RPB), dim3(kThreads), 0, s, rp);
   } else if (p->BN == 64) {
     constexpr int RPB = 64;
