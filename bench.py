@@ -287,6 +287,138 @@ def configs_check(torch, fo, Pipeline, dev, streams, scratch, steps=20, warmup=5
     return out
 
 
+def _time_partitions(torch, Pipeline, plans, dA, dB, dpeer, streams, steps, rounds=3, warmup=2):
+    """Median end of communication (GEMM start to the consumer's end, ms) of each plan's pipeline, timed in
+    `rounds` interleaved rounds whose order rotates, after a common warm-up: a partition timed first after
+    another workload's passes ran up to 8% slow."""
+    pipes = [Pipeline(p, dA, dB, dpeer, streams=streams) for p in plans]
+    for _ in range(3 * warmup):
+        for pipe in pipes:
+            pipe.step()
+    per = [[] for _ in pipes]
+    n = len(pipes)
+    for r in range(rounds):
+        for k in range(n):
+            i = (k + r * max(1, n // rounds)) % n
+            pipe = pipes[i]
+            for _ in range(warmup):
+                pipe.step()
+            evs = [{key: _event_pairs(torch, 1)[0] for key in ("gemm", "consume", "post")} for _ in range(steps)]
+            for e in evs:
+                pipe.step(events=e)
+            pipe.join()
+            torch.cuda.synchronize()
+            if int(pipe.status.item()) != 0:
+                raise SystemExit(f"consumer reported status {int(pipe.status.item())}")
+            per[i].append(float(np.median([e["gemm"][0].elapsed_time(e["consume"][1]) for e in evs])))
+    for pipe in pipes:
+        pipe.close()
+    return [float(np.median(x)) for x in per]
+
+
+def _cut_mask(comp) -> int:
+    """Waves per group -> cut mask (bit i: a group ends after wave i + 1), the index of fo_plan_search's
+    per-partition predictions."""
+    mask, end = 0, 0
+    for c in comp[:-1]:
+        end += c
+        mask |= 1 << (end - 1)
+    return mask
+
+
+def moe_search_check(torch, fo, Pipeline, dev, streams, steps=10, warmup=3, samples=8):
+    """Predictive partition search on the MoE shape, whose waves leave too many partitions to run them all
+    (deep-dive 三 › 调优挑战: the tuning cost grows as 2^(T-1); 四 › 在线阶段: the search replaces it).
+
+    fo_plan_search scores every partition from the GEMM's duration and a consumer latency curve (sampled up to
+    the MoE output's size, at the MoE row width); its choice then runs in the pipeline beside a fixed set of
+    partitions (one group; one wave per group; even groups of 2, 4 and 8 waves; one small group first or last)
+    and `samples` random ones, and the measured end of communication (GEMM start to the consumer's end) ranks
+    them.  Inputs are drawn on the device (throughput does not depend on the values)."""
+    from workloads import WORKLOADS, moe_routing
+    w = WORKLOADS["moe_a2a"]
+    m_per, tok = moe_routing(w)
+    row_dest = tok // (w.tokens // w.ranks)
+    M = sum(m_per)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed_base)
+    std = w.dist[1]
+    dA = (torch.randn(M * w.K, device=dev, generator=g) * std).to(torch.bfloat16).view(torch.int16)
+    dB = (torch.randn(len(m_per) * w.N * w.K, device=dev, generator=g) * std).to(torch.bfloat16).view(torch.int16)
+    dpeer = (torch.randn(M * w.N, device=dev, generator=g) * std).to(torch.bfloat16).view(torch.int16)
+    s = streams[0]
+
+    def plan_of(comp=None):
+        return fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp,
+                       mode=w.mode, ranks=w.ranks, row_dest=row_dest)
+    base = plan_of()
+    T = base.T
+    C = torch.empty(M * w.N, dtype=torch.int16, device=dev)
+    for _ in range(3):
+        base.gemm_plain(dA, dB, C, stream=s)
+    gemm_ms = float(np.median([_time_kernel(torch, lambda st: base.gemm_plain(dA, dB, C, stream=st), s, 1)
+                               for _ in range(5)]))
+    del C
+    curve_b, curve_s = [], []
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for rows in (64, 256, 1024, 2048, 4096, 8192):
+        probe = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W)
+        cp = fo.Plan(rows, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=(probe.T,))
+        probe.close()
+        x = torch.zeros(cp.M * cp.N, dtype=torch.int16, device=dev)
+        y = torch.empty_like(x)
+        ready = cp.new_sig(dev)
+        cp.flag_of(ready).fill_(1)
+        ms = float(np.median([_time_kernel(torch, lambda st: cp.consume_group_gated(x, x, y, ready, 1, status,
+                                                                                    stream=st),
+                                           s, 1) for _ in range(5)]))
+        curve_b.append(2.0 * cp.M * cp.N)
+        curve_s.append(ms * 1e-3)
+        cp.close()
+        del x, y
+    pred, pred_s, all_s = base.search(gemm_ms * 1e-3, curve_b, curve_s, with_all=True)
+    base.close()
+    fixed = [(T,), (1,) * T, (2,) * (T // 2) + (1,) * (T % 2), (4,) * (T // 4) + ((T % 4,) if T % 4 else ()),
+             (8,) * (T // 8) + ((T % 8,) if T % 8 else ()), (1, T - 1), (T - 1, 1)]
+    rng = np.random.Generator(np.random.PCG64(w.seed_base + 5))
+    rand = []
+    for _ in range(samples):
+        cuts = rng.integers(0, 2, size=T - 1)
+        comp, run = [], 0
+        for i in range(T):
+            run += 1
+            if i == T - 1 or cuts[i]:
+                comp.append(run)
+                run = 0
+        rand.append(tuple(comp))
+    cands = []
+    for c in [tuple(pred)] + fixed + rand:
+        if c not in cands:
+            cands.append(c)
+    plans = [plan_of(c) for c in cands]
+    meas = _time_partitions(torch, Pipeline, plans, dA, dB, dpeer, streams, steps, warmup=warmup)
+    for p_ in plans:
+        p_.close()
+    rows_out = [(c, all_s[_cut_mask(c)] * 1e3, m) for c, m in zip(cands, meas)]
+    del dA, dB, dpeer
+    best = min(rows_out, key=lambda r: r[2])
+    pick = rows_out[0]
+    order = sorted(rows_out, key=lambda r: r[2])
+    return {
+        "workload": f"{w.name}: M={M} N={w.N} K={w.K}, {w.BM}x{w.BN} tiles, T={T}, {1 << (T - 1)} partitions, "
+                    f"gated consumer",
+        "gemm_plain_us": round(gemm_ms * 1e3, 1),
+        "curve_bytes": curve_b, "curve_us": [round(x * 1e6, 2) for x in curve_s],
+        "predicted_best": list(pred), "predicted_us": round(pred_s * 1e6, 1),
+        "measured": len(rows_out), "best_of_measured": list(best[0]), "best_of_measured_us": round(best[2] * 1e3, 1),
+        "predicted_choice_measured_us": round(pick[2] * 1e3, 1),
+        "regret_vs_best_of_measured": round(pick[2] / best[2] - 1.0, 4),
+        "rank_of_predicted_choice": 1 + [r[0] for r in order].index(pick[0]),
+        "candidates": [{"groups": list(c), "predicted_us": round(p * 1e3, 1), "measured_us": round(m * 1e3, 1)}
+                       for c, p, m in rows_out],
+    }
+
+
 def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
     """Predictive partition search against measurement on the 4-wave prefill workload.
 
@@ -337,24 +469,13 @@ def search_check(torch, fo, Pipeline, dev, streams, steps=20, warmup=5):
                 run = 0
         return tuple(out)
 
-    rows = []
-    for mask in range(1 << (base.T - 1)):
-        comp = comp_of(mask, base.T)
-        plan = fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=comp)
-        pipe = Pipeline(plan, dA, dB, dpeer, streams=streams)
-        for _ in range(warmup):
-            pipe.step()
-        evs = [{k: _event_pairs(torch, 1)[0] for k in ("gemm", "consume", "post")} for _ in range(steps)]
-        for e in evs:
-            pipe.step(events=e)
-        pipe.join()
-        torch.cuda.synchronize()
-        if int(pipe.status.item()) != 0:
-            raise SystemExit(f"consumer reported {fo.status_string(int(pipe.status.item()))}")
-        meas = float(np.median([e["gemm"][0].elapsed_time(e["consume"][1]) for e in evs]))
-        pipe.close()
-        plan.close()
-        rows.append((comp, all_s[mask] * 1e3, meas))
+    comps = [comp_of(mask, base.T) for mask in range(1 << (base.T - 1))]
+    plans = [fo.Plan(m_per, w.N, w.K, w.dtype, BM=w.BM, BN=w.BN, swizzle=w.S, wave_size=w.W, composition=c)
+             for c in comps]
+    meas = _time_partitions(torch, Pipeline, plans, dA, dB, dpeer, streams, steps, warmup=warmup)
+    for p_ in plans:
+        p_.close()
+    rows = [(c, all_s[mask] * 1e3, m) for mask, (c, m) in enumerate(zip(comps, meas))]
     T = base.T
     base.close()
     best_m = min(rows, key=lambda r: r[2])
@@ -838,6 +959,7 @@ def main():
         line["configs"] = configs_check(torch, fo, Pipeline, dev, streams, scratch)
     if not a.no_search:
         line["search"] = search_check(torch, fo, Pipeline, dev, streams)
+        line["search_moe"] = moe_search_check(torch, fo, Pipeline, dev, streams)
     # release every device object before the interpreter exits
     torch.cuda.synchronize()
     for st in streams:
