@@ -30,3 +30,18 @@ def test_traffic_record_is_tied_to_the_kernel_sources():
     else:
         assert rec is None
     assert bench.committed_traffic("no_such_workload") is None
+
+
+def test_partition_cut_masks_index_the_searchs_predictions():
+    """The MoE search check reads each partition's prediction at its cut mask (bit i: a group ends after wave
+    i + 1), the order in which fo_plan_search and the oracle list their candidates."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from oracle import enumerate_compositions
+    for T in (1, 2, 5, 9):
+        comps = list(enumerate_compositions(T))
+        assert len(comps) == 1 << (T - 1)
+        for mask, comp in enumerate(comps):
+            assert bench._cut_mask(comp) == mask
+    assert bench._cut_mask((17,)) == 0 and bench._cut_mask((1,) * 17) == (1 << 16) - 1
+    assert bench._cut_mask((8, 8, 1)) == (1 << 7) | (1 << 15)
